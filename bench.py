@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark one sparse-MoE sub-layer forward pass on one MI355X.
+
+A step is the whole pass: router -> dispatch -> expert up -> expert down
+(-> shared experts) -> combine -> routing statistics, on one batch of
+synthetic inputs already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload default]
+
+Per-call durations come from HIP events recorded on the stream the kernels
+run on (torch's current stream, which every call is given).  The dominant
+kernel is the bf16 grouped GEMM (two launches per step: expert up and expert
+down); its roofline figure uses the algorithmic FLOPs of one launch,
+2 * rows * d * F for the kept rows, over the measured average launch time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec at 1 MI355X; grouped-FFN MFMA util %; dispatch GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+WORKLOADS = {
+    "tiny": "TINY", "default": "DEFAULT", "switch_zipf": "SWITCH_ZIPF",
+    "fine_shared": "FINE_SHARED", "large_credit": "LARGE_CREDIT",
+}
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="default", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import threadpoolctl
+    import oracle
+    import synth
+    Ts = w.T if w.T <= 4096 else 512
+    inp = synth.draw(w.with_(T=Ts))
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": Ts * reps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full float64 oracle pass(es) over a batch of {Ts} tokens of this workload "
+                      f"({el:.1f} s)"}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer has no multi-GPU path (see DESIGN.md, "
+              "sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+    import synth
+    from synth.device import to_torch
+    from sparse_mixture_experts_10_amd import MoELayer
+
+    w = getattr(synth, WORKLOADS[args.workload])
+    inp = synth.draw(w)
+    t = to_torch(inp, "cuda")
+    shared = (t["sW1"], t["sb1"], t["sW2"], t["sb2"]) if w.n_shared else None
+    layer = MoELayer(t["W_g"], t["W1"], t["b1"], t["W2"], t["b2"], k=w.k, act=w.act,
+                     capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
+                     alpha=w.alpha, beta=w.beta, credit=w.credit)
+    x = t["x"]
+    o = layer.allocate(w.T)
+    calls = [("router", lambda: layer.router(x, o)), ("dispatch", lambda: layer.dispatch(x, o)),
+             ("expert_up", lambda: layer.expert_up(o)), ("expert_down", lambda: layer.expert_down(o)),
+             ("shared", lambda: layer.shared_experts(x, o)), ("combine", lambda: layer.combine(o)),
+             ("stats", lambda: layer.stats(o))]
+    if not w.n_shared:
+        calls = [c for c in calls if c[0] != "shared"]
+
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(K):
+        ev[s][0].record()
+        for i, (_, fn) in enumerate(calls):
+            fn()
+            ev[s][i + 1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / K
+    per_call = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])) * 1e3
+                for i, (name, _) in enumerate(calls)}   # microseconds
+
+    # algorithmic work
+    T, d, E, k, F = w.T, w.d, w.E, w.k, w.F
+    rows = int(o.expert_offset[-1])
+    eb = 2 if w.dtype == "bf16" else 4
+    gemm_flops = 2.0 * rows * d * F                       # one launch (up or down)
+    gemm_us = 0.5 * (per_call["expert_up"] + per_call["expert_down"])
+    achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
+    router_bytes = T * d * eb + E * d * 4 + T * E * 4 + T * 4 + 2 * T * k * 4
+    dispatch_bytes = T * d * eb + rows * d * eb + T * k * 4 * 3 + rows * 4
+    combine_bytes = rows * d * eb + T * d * eb + 2 * T * k * 4 + (T * d * eb if w.n_shared else 0)
+
+    def gbps(b, us):
+        return b / (us * 1e-6) / 1e9
+
+    kernels = {
+        "router": {"us": per_call["router"], "GB/s": gbps(router_bytes, per_call["router"])},
+        "dispatch": {"us": per_call["dispatch"], "GB/s": gbps(dispatch_bytes, per_call["dispatch"])},
+        "expert_up": {"us": per_call["expert_up"],
+                      "TFLOP/s": gemm_flops / (per_call["expert_up"] * 1e-6) / 1e12},
+        "expert_down": {"us": per_call["expert_down"],
+                        "TFLOP/s": gemm_flops / (per_call["expert_down"] * 1e-6) / 1e12},
+        "combine": {"us": per_call["combine"], "GB/s": gbps(combine_bytes, per_call["combine"])},
+        "stats": {"us": per_call["stats"]},
+    }
+    if w.n_shared:
+        kernels["shared"] = {"us": per_call["shared"],
+                             "TFLOP/s": 4.0 * T * d * F * w.n_shared / (per_call["shared"] * 1e-6) / 1e12}
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "d": d, "E": E, "k": k, "F": F, "act": w.act,
+                   "capacity_factor": None if w.capacity_factor is None else str(w.capacity_factor),
+                   "n_shared": w.n_shared, "kept_rows": rows},
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (expert up + down, 2 launches/step)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "mfma_util_pct": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "dispatch_GBps": kernels["dispatch"]["GB/s"],
+        "kernels": kernels,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

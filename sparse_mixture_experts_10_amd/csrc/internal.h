@@ -1,0 +1,63 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+// All of them enqueue on `st` and return the launch status; none blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kDispatchChunk = 64;    // tokens per dispatch chunk (one wavefront)
+constexpr int kStatsTokens = 256;     // tokens per statistics partial block
+constexpr int kGemmBN = 128;          // N tile of the bf16 grouped GEMM
+constexpr int kGemmBM = 128;          // M tile of the bf16 grouped GEMM
+constexpr int kGemmF32BN = 64;        // N tile of the fp32 grouped GEMM
+constexpr int kGemmF32BM = 64;        // M tile of the fp32 grouped GEMM
+
+hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
+                         const float* bg, const float* bsel, int E, int k, float* logits,
+                         float* lse, int32_t* idx, float* gate, hipStream_t st);
+
+// workspace: hist [nchunks*E] int32 then chunk_base [nchunks*E] int32
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t capacity,
+                           const void* x, int elem_bytes, int d, int32_t* count,
+                           int32_t* offset, int32_t* slot, int32_t* row, int32_t* row_token,
+                           void* x_disp, int32_t* ws_hist, int32_t* ws_base, hipStream_t st);
+
+// One grouped GEMM pass  C[r, n] = epi( sum_k A[r, k] * B[g(r)][n, k] ).
+struct GemmArgs {
+  const void* A;             // [rows, K]
+  const int32_t* group_offset;  // [G+1] device, or nullptr: one group of dense_M rows
+  int G;
+  int64_t dense_M;
+  int64_t max_rows;          // rows >= max_rows are neither read nor written
+  const void* B;             // [G][N][K] (or [S][N][Kseg] when S > 1, one group)
+  int N, K;
+  int S, Kseg;               // K = S * Kseg; B segment s holds columns [s*Kseg, (s+1)*Kseg)
+  const void* bias;          // [G][N], or [S][N] summed over s when S > 1
+  void* C;                   // [rows, N]
+  int act;                   // activation, or -1 for none
+  float* sq_part;            // [max_rows][n_tiles] partial sum of squares, or nullptr
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+hipError_t launch_sq_reduce(const float* sq_part, int n_tiles, const int32_t* group_offset, int G,
+                            int64_t max_rows, float* sq, hipStream_t st);
+
+hipError_t launch_combine(const void* expert_out, const int32_t* row, const float* gate,
+                          const void* shared_out, int64_t T, int k, int d_out, bool bf16,
+                          void* y, hipStream_t st);
+
+// workspace: partial [nblocks][E+1] double
+hipError_t launch_stats(const float* logits, const float* lse, const int32_t* idx,
+                        const float* gate, const int32_t* count, int64_t T, int E, int k,
+                        float alpha, float beta, float* f, float* Pm, float* losses,
+                        const float* sq, const int32_t* row, const int32_t* offset,
+                        const int32_t* row_token, float* credit, float* mean_credit,
+                        double* ws_partial, hipStream_t st);
+
+}  // namespace moe

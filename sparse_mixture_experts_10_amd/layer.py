@@ -1,0 +1,152 @@
+"""One sparse-MoE sub-layer forward pass as a sequence of C-ABI calls.
+
+    router_topk -> dispatch -> expert_up -> expert_down (-> shared_ffn) -> combine -> route_stats
+
+This is the forward entry of page "Code Walkthrough -- SER" (the layer's
+forward runs gate, route, the selected experts and the gate-weighted combine),
+with the statistics of page "Appendix C -- Acronyms & Symbols" (Balancing) and
+the credit of the expert-credit diagram page, panel (b).  Python only
+allocates buffers (torch) and passes pointers; every step runs in HIP.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from fractions import Fraction
+from typing import Optional, Tuple
+
+import torch
+
+from . import api
+
+
+@dataclass
+class MoEOutputs:
+    T: int
+    capacity: int               # -1 = no cap
+    max_rows: int
+    logits: torch.Tensor        # [T, E] fp32
+    lse: torch.Tensor           # [T] fp32
+    topk_idx: torch.Tensor      # [T, k] int32
+    topk_gate: torch.Tensor     # [T, k] fp32
+    expert_count: torch.Tensor  # [E] int32
+    expert_offset: torch.Tensor  # [E+1] int32
+    slot: torch.Tensor          # [T, k] int32
+    row: torch.Tensor           # [T, k] int32
+    row_token: torch.Tensor     # [rows] int32
+    x_disp: torch.Tensor        # [rows, d]
+    hidden: torch.Tensor        # [rows, F]
+    y_disp: torch.Tensor        # [rows, d]
+    sqnorm: Optional[torch.Tensor]
+    shared_hidden: Optional[torch.Tensor]
+    shared_out: Optional[torch.Tensor]
+    y: torch.Tensor             # [T, d]
+    f: torch.Tensor             # [E]
+    P: torch.Tensor             # [E]
+    losses: torch.Tensor        # [3] = L_aux, L_z, sum
+    credit: Optional[torch.Tensor]
+    mean_credit: Optional[torch.Tensor]
+    ws_dispatch: torch.Tensor
+    ws_ffn: Optional[torch.Tensor]
+    ws_stats: torch.Tensor
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+class MoELayer:
+    """Parameters on the device plus the calls of one forward pass.
+
+    W_g [E, d] fp32, b_g / b_sel [E] fp32 or None; W1 [E, F, d], b1 [E, F],
+    W2 [E, d, F], b2 [E, d] in the layer dtype (bf16 or fp32); shared =
+    (W1 [S, F, d], b1 [S, F], W2 [S, d, F], b2 [S, d]) or None.
+    capacity_factor: a Fraction (or anything Fraction accepts), None = no cap.
+    """
+
+    def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
+                 b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
+                 alpha: float = 0.01, beta: float = 1e-3, credit: bool = False):
+        self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
+        self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
+        self.shared = shared
+        self.k, self.act = k, act
+        self.cf = None if capacity_factor is None else Fraction(capacity_factor)
+        self.alpha, self.beta, self.credit = alpha, beta, credit
+        self.E, self.F, self.d = W1.shape
+        self.dtype = W1.dtype
+        self.device = W1.device
+
+    def capacity(self, T: int) -> int:
+        if self.cf is None:
+            return -1
+        return api.moe_capacity(self.cf.numerator, self.cf.denominator, self.k, T, self.E)
+
+    def allocate(self, T: int) -> MoEOutputs:
+        E, k, d, F, dev, dt = self.E, self.k, self.d, self.F, self.device, self.dtype
+        C = self.capacity(T)
+        max_rows = T * k if C < 0 else min(T * k, E * C)
+        rows = max(max_rows, 1)
+        i32, f32 = torch.int32, torch.float32
+        e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)
+        S = 0 if self.shared is None else self.shared[0].shape[0]
+        return MoEOutputs(
+            T=T, capacity=C, max_rows=max_rows,
+            logits=e(T, E, dtype=f32), lse=e(T, dtype=f32),
+            topk_idx=e(T, k, dtype=i32), topk_gate=e(T, k, dtype=f32),
+            expert_count=e(E, dtype=i32), expert_offset=e(E + 1, dtype=i32),
+            slot=e(T, k, dtype=i32), row=e(T, k, dtype=i32), row_token=e(rows, dtype=i32),
+            x_disp=e(rows, d), hidden=e(rows, F), y_disp=e(rows, d),
+            sqnorm=e(rows, dtype=f32) if self.credit else None,
+            shared_hidden=e(T, S * F) if S else None, shared_out=e(T, d) if S else None,
+            y=e(T, d), f=e(E, dtype=f32), P=e(E, dtype=f32), losses=e(3, dtype=f32),
+            credit=e(T, k, dtype=f32) if self.credit else None,
+            mean_credit=e(E, dtype=f32) if self.credit else None,
+            ws_dispatch=_ws(api.moe_workspace_bytes(api.OP_DISPATCH, T=T, E=E), dev),
+            ws_ffn=_ws(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dev) if self.credit else None,
+            ws_stats=_ws(api.moe_workspace_bytes(api.OP_STATS, T=T, E=E), dev),
+        )
+
+    def forward(self, x: torch.Tensor, out: Optional[MoEOutputs] = None, stream=None) -> MoEOutputs:
+        T = x.shape[0]
+        o = self.allocate(T) if out is None else out
+        if o.T != T:
+            raise ValueError("output buffers were allocated for another batch size")
+        self.router(x, o, stream)
+        self.dispatch(x, o, stream)
+        self.expert_up(o, stream)
+        self.expert_down(o, stream)
+        self.shared_experts(x, o, stream)
+        self.combine(o, stream)
+        self.stats(o, stream)
+        return o
+
+    # one method per C-ABI call, in forward order
+    def router(self, x, o: MoEOutputs, stream=None) -> None:
+        api.moe_router_topk(x, self.W_g, self.b_g, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
+                            o.topk_gate, stream)
+
+    def dispatch(self, x, o: MoEOutputs, stream=None) -> None:
+        api.moe_dispatch(o.topk_idx, self.E, o.capacity, x, o.expert_count, o.expert_offset, o.slot,
+                         o.row, o.row_token, o.x_disp, o.ws_dispatch, stream)
+
+    def expert_up(self, o: MoEOutputs, stream=None) -> None:
+        if o.max_rows > 0:
+            api.moe_expert_up(o.x_disp, o.expert_offset, o.max_rows, self.W1, self.b1, self.act, o.hidden,
+                              o.sqnorm, o.ws_ffn, stream)
+
+    def expert_down(self, o: MoEOutputs, stream=None) -> None:
+        if o.max_rows > 0:
+            api.moe_expert_down(o.hidden, o.expert_offset, o.max_rows, self.W2, self.b2, o.y_disp, stream)
+
+    def shared_experts(self, x, o: MoEOutputs, stream=None) -> None:
+        if self.shared is not None:
+            sW1, sb1, sW2, sb2 = self.shared
+            api.moe_shared_ffn(x, sW1, sb1, sW2, sb2, self.act, o.shared_hidden, o.shared_out, stream)
+
+    def combine(self, o: MoEOutputs, stream=None) -> None:
+        api.moe_combine(o.y_disp, o.row, o.topk_gate, o.shared_out, o.y, stream)
+
+    def stats(self, o: MoEOutputs, stream=None) -> None:
+        api.moe_route_stats(o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, self.alpha,
+                            self.beta, o.f, o.P, o.losses, o.sqnorm, o.row, o.expert_offset,
+                            o.row_token, o.credit, o.mean_credit, o.ws_stats, stream)
