@@ -314,7 +314,7 @@ def forward(inp: Inputs, tokens: Optional[Sequence[int]] = None,
     C = capacity(w.capacity_factor, k, T, E)
     disp = dispatch(idx, E, C)
 
-    tok = np.arange(T) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)))
+    tok = np.arange(T) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)), dtype=np.int64)
     want = np.zeros(T, bool)
     want[tok] = True
     expert_out: Dict[int, np.ndarray] = {}
