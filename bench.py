@@ -7,8 +7,10 @@ synthetic inputs already resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload default]
 
-Per-call durations come from HIP events recorded on the stream the kernels
-run on (torch's current stream, which every call is given).  The dominant
+Steps are timed as K replays of one HIP graph holding the whole pass.  Per-call
+durations come from HIP events recorded around each call on the stream the
+kernels run on (torch's current stream, which every call is given), with the
+queue kept full so the events measure the GPU and not host launch latency.  The dominant
 kernel is the bf16 grouped GEMM (two launches per step: expert up and expert
 down); its roofline figure uses the algorithmic FLOPs of one launch,
 2 * rows * d * F for the kept rows, over the measured average launch time.
@@ -113,29 +115,49 @@ def main():
     if not w.n_shared:
         calls = [c for c in calls if c[0] != "shared"]
 
-    for _ in range(args.warmup):
+    def step():
         for _, fn in calls:
             fn()
-    torch.cuda.synchronize()
 
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # Whole steps: one step captured as a HIP graph and replayed K times.  A
+    # sleep kernel keeps the GPU busy while the host queues the replays, so the
+    # events see back-to-back steps, not host launch latency.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, stop = ev(), ev()
     wall0 = time.perf_counter()
+    torch.cuda._sleep(int(2.4e9 * 200e-6 * K))
     start.record()
-    for s in range(K):
-        ev[s][0].record()
-        for i, (_, fn) in enumerate(calls):
-            fn()
-            ev[s][i + 1].record()
+    for _ in range(K):
+        graph.replay()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / K
-    per_call = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])) * 1e3
+    ms_step = start.elapsed_time(stop) / K
+
+    # Per call: events around each call of K eager steps, queue pre-filled the same way.
+    evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 600e-6 * K))
+    for s in range(K):
+        evs[s][0].record()
+        for i, (_, fn) in enumerate(calls):
+            fn()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    per_call = {name: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)])) * 1e3
                 for i, (name, _) in enumerate(calls)}   # microseconds
+    ms_step_eager = sum(per_call.values()) / 1e3
 
     # algorithmic work
     T, d, E, k, F = w.T, w.d, w.E, w.k, w.F
@@ -173,6 +195,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_calls": ms_step_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

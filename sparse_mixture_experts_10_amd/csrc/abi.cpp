@@ -189,7 +189,7 @@ static hipError_t run_up(const void* a, const int32_t* group_offset, int32_t G, 
   g.act = act; g.sq_part = hidden_sqnorm ? (float*)ws : nullptr;
   hipError_t e = bf16 ? launch_gemm_bf16(g, stream) : launch_gemm_f32(g, stream);
   if (e != hipSuccess || hidden_sqnorm == nullptr) return e;
-  const int tiles = bf16 ? (F + kGemmBN - 1) / kGemmBN : (F + kGemmF32BN - 1) / kGemmF32BN;
+  const int tiles = bf16 ? gemm_bf16_n_tiles(g) : (F + kGemmF32BN - 1) / kGemmF32BN;
   return launch_sq_reduce((const float*)ws, tiles, group_offset, G, max_rows, hidden_sqnorm, stream);
 }
 

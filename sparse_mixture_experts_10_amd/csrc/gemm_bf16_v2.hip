@@ -1,0 +1,266 @@
+// Pipelined bf16 grouped GEMM for gfx950 (expert up / down passes).
+//
+// Same contract as the first bf16 path in grouped_gemm.hip (C = epi(A B^T)
+// over ragged groups, see GemmArgs), built for throughput:
+//  * operands go global -> LDS directly (global_load_lds_dwordx4: each lane's
+//    16 bytes land at M0 + 16 * lane), no register staging;
+//  * an NS-stage LDS ring of K = 32 slabs, loads issued NS-1 slabs ahead, one
+//    barrier per slab;
+//  * slab rows are 64 bytes (K = 32) with their 16-byte chunks permuted per
+//    row (swz) so MFMA operand reads run conflict-free, while each 4 lanes of
+//    a load still fetch one row's 64 contiguous bytes;
+//  * block tile BM x BN, 4 waves in 2 x 2, each wave (BM/2) x (BN/2) of
+//    v_mfma_f32_16x16x32_bf16 tiles; the output is staged through LDS in
+//    32-row chunks for 16-byte stores.
+// Requires K % 32 == 0 (and, for S > 1, Kseg % 32 == 0).
+
+#include "common.h"
+#include "internal.h"
+#include "gemm_tiles.h"
+
+namespace moe {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Slab rows are 64 bytes (32 bf16 of K) with their four 16-byte chunks
+// permuted: logical chunk c of row r sits at chunk c ^ swz(r).  An MFMA operand
+// read (16 lanes = 16 consecutive rows at one logical chunk) then takes the
+// minimum 4 LDS cycles per ds_read_b128; rows unpermuted, or permuted by
+// r & 3 or by (r >> 2) & 3, take 8 (measured on MI355X with LDS
+// bank-conflict counters).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+__device__ __forceinline__ void slab_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int BM, int BN, int WGM, int WGN, int NS, bool SEG>
+struct V2 {
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;     // waves, threads
+  static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave tile
+  static constexpr int TM = WM / 16, TN = WN / 16;       // MFMA tiles per wave
+  static constexpr int SLAB = (BM + BN) * 64;            // bytes per stage
+  static constexpr int LPW = (BM + BN) / (16 * NW);      // load instructions per wave per stage
+  static constexpr int SR = 16 * WGM;                    // output rows staged per pass
+  static constexpr int LDC = (SR * (BN + 8) * 2 <= SLAB) ? BN + 8 : BN;  // staged row (bf16)
+  static_assert((BM + BN) % (16 * NW) == 0, "slab rows must split evenly over the waves");
+  static_assert(SR * LDC * 2 <= SLAB, "staged output rows must fit in one stage buffer");
+  static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
+};
+
+// One LDS array per stage: distinct objects let the compiler see that reading
+// one stage does not alias the loads in flight into the others.
+template <int BM, int BN, int WGM, int WGN, int NS, int MINB, bool SEG>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(GemmArgs p) {
+  using C = V2<BM, BN, WGM, WGN, NS, SEG>;
+  constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st1[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st2[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? C::SLAB : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? C::SLAB : 16];
+  __shared__ int s_info[4];
+  __shared__ float s_sq[WGN][BM];
+  char* const stages[6] = {st0, st1, st2, st3, st4, st5};
+
+  const int n_tiles = (p.N + BN - 1) / BN;
+  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
+  if (tl.M <= 0) return;  // uniform
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int N = p.N, K = p.K;
+  const int n0 = tl.nt * BN;
+  const bf16_t* A = (const bf16_t*)p.A;
+  const bf16_t* B = (const bf16_t*)p.B;
+
+  // ---- this lane's load slots: instruction j = wave + NW i fills slab rows
+  // 16 j .. 16 j + 15 (1 KB); lane l fills row 16 j + l / 4, physical chunk l % 4,
+  // so each 4 lanes fetch one row's 64 contiguous bytes
+  const bf16_t* src[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = 16 * (wave + NW * i) + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(row);  // logical chunk stored here
+    if (row < BM) {
+      const int r = row < tl.M ? row : tl.M - 1;
+      src[i] = A + (tl.row0 + r) * (int64_t)K + chunk * 8;
+    } else {
+      const int nr = row - BM;
+      const int n = (n0 + nr < N) ? n0 + nr : N - 1;
+      src[i] = SEG ? B + (int64_t)n * p.Kseg + chunk * 8
+                   : B + ((int64_t)tl.g * N + n) * K + chunk * 8;
+    }
+  }
+  const int nk = K / 32;
+  auto issue = [&](int kt, int stage) {
+    const int k = (kt < nk ? kt : nk - 1) * 32;  // past the end: harmless reload
+    char* base = stages[stage];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int row0 = 16 * (wave + NW * i);
+      int64_t off = k;
+      if (SEG && row0 >= BM) {
+        const int s = k / p.Kseg;
+        off = (int64_t)s * N * p.Kseg + (k - s * p.Kseg);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + off), (lds_ptr_t)(base + row0 * 64), 16, 0, 0);
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // operand read offsets (bytes within a slab): lane (fr, fc) reads row fr
+  // of its 16-row tile at logical k-chunk fc
+  const int fr = lane & 15, fc = lane >> 4;
+  int a_rd[TM], b_rd[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int R = wm * C::WM + i * 16 + fr;
+    a_rd[i] = R * 64 + ((fc ^ swz(R)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int R = BM + wn * C::WN + j * 16 + fr;
+    b_rd[j] = R * 64 + ((fc ^ swz(R)) << 4);
+  }
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+
+  auto step = [&](int kt, int stage) {
+    wait_vmcnt<(NS - 2) * LPW>();   // this wave's loads of step kt have landed
+    slab_barrier();                  // ... and every other wave's
+    issue(kt + NS - 1, (stage + NS - 1) % NS);
+    const char* base = stages[stage];
+    bf16x8_t a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[j]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) step(kt + s, s);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (kt + s < nk) step(kt + s, s);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- epilogue: lane holds C[wm*WM + i*16 + 4*fc + r][wn*WN + j*16 + fr] ----
+  const bf16_t* bias = (const bf16_t*)p.bias;
+  float bcol[TN];
+  bool ncol_ok[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + wn * C::WN + j * 16 + fr;
+    ncol_ok[j] = n < N;
+    float bv = 0.f;
+    if (ncol_ok[j] && bias != nullptr) {
+      if (SEG) {
+        for (int q = 0; q < p.S; ++q) bv += bf16_to_f32(bias[(int64_t)q * N + n]);
+      } else {
+        bv = bf16_to_f32(bias[(int64_t)tl.g * N + n]);
+      }
+    }
+    bcol[j] = bv;
+  }
+  const bool want_sq = p.sq_part != nullptr;
+  bf16_t* Cs = (bf16_t*)st0;
+  bf16_t* Cg = (bf16_t*)p.C;
+  // pass i stages row tile i of every wave row (SR rows: staging row
+  // 16 * wm + q holds tile row wm * WM + 16 i + q) and stores them
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[i][j][r] + bcol[j];
+        if (p.act >= 0) v = apply_act(p.act, v);
+        if (ncol_ok[j]) rs[r] += v * v;
+        Cs[(wm * 16 + fc * 4 + r) * C::LDC + wn * C::WN + j * 16 + fr] = f32_to_bf16(v);
+      }
+    }
+    if (want_sq) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sum = rs[r];
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        sum += __shfl_xor(sum, 4, 64);
+        sum += __shfl_xor(sum, 8, 64);
+        if (fr == 0) s_sq[wn][wm * C::WM + i * 16 + fc * 4 + r] = sum;
+      }
+    }
+    __syncthreads();
+    constexpr int VPR = BN / 8;  // 16-byte vectors per staged row
+#pragma unroll
+    for (int v = tid; v < C::SR * VPR; v += NT) {
+      const int sr = v / VPR, cv = v % VPR;
+      const int m = (sr >> 4) * C::WM + i * 16 + (sr & 15);
+      const int n = n0 + cv * 8;
+      if (m < tl.M && n < N)
+        *(vec16*)(Cg + (tl.row0 + m) * (int64_t)N + n) = *(const vec16*)(Cs + sr * C::LDC + cv * 8);
+    }
+    __syncthreads();
+  }
+  if (want_sq)
+    for (int m = tid; m < tl.M; m += NT) {
+      float sum = 0.f;
+      for (int q = 0; q < WGN; ++q) sum += s_sq[q][m];
+      p.sq_part[(tl.row0 + m) * (int64_t)n_tiles + tl.nt] = sum;
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int MINB>
+static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
+  const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
+  if (rows <= 0) return hipSuccess;
+  const int64_t mt = (rows + BM - 1) / BM + (a.group_offset ? a.G : 0);
+  const dim3 grid((unsigned)grid_blocks(mt, (a.N + BN - 1) / BN));
+  const dim3 block(64 * WGM * WGN);
+  if (a.S > 1)
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, MINB, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, MINB, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+bool gemm_v2_supported(const GemmArgs& a) {
+  return a.K % 32 == 0 && (a.S <= 1 || a.Kseg % 32 == 0);
+}
+
+hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
+  if (tile == 256) return launch_v2<256, 128, 2, 2, 3, 2>(a, st);
+  return launch_v2<128, 128, 2, 2, 4, 2>(a, st);
+}
+
+}  // namespace moe

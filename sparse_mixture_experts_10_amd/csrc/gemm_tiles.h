@@ -1,0 +1,97 @@
+// Ragged tile mapping shared by the grouped GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Tile {
+  int g;
+  int64_t row0;
+  int M;   // valid rows in this tile (0: block has no work)
+  int nt;  // N-tile index
+};
+
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin by id
+
+// Maps blockIdx.x to a (group, row tile, N tile).  The tile list is row-tile
+// major over the groups in order (so consecutive tiles share A rows and the
+// group's weights) and each XCD takes one contiguous band of it, keeping a
+// band's operands in that XCD's L2.  Wave 0 builds the per-group row-tile
+// prefix from the device-side offsets; the result goes through LDS.
+template <int BM>
+__device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int G, int64_t dense_M, int64_t max_rows,
+                          int n_tiles, int* s_info) {
+  Tile tl;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int total_m, incl = 0, local = 0, g0 = 0, gpl = 1;
+    if (goff == nullptr) {
+      total_m = (int)((dense_M + BM - 1) / BM);
+    } else {
+      gpl = (G + 63) / 64;  // groups per lane (<= 4)
+      g0 = lane * gpl;
+      for (int q = 0; q < gpl; ++q) {
+        const int g = g0 + q;
+        if (g < G) local += (goff[g + 1] - goff[g] + BM - 1) / BM;
+      }
+      incl = local;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_up(incl, m, 64);
+        if (lane >= m) incl += o;
+      }
+      total_m = __shfl(incl, 63, 64);
+    }
+    const int64_t total = (int64_t)total_m * n_tiles;
+    const int64_t band = (total + kXcds - 1) / kXcds;
+    const int64_t b = blockIdx.x;
+    const int64_t i = b / kXcds;
+    const int64_t L = (b % kXcds) * band + i;
+    const bool work = i < band && L < total;
+    const int mt = work ? (int)(L / n_tiles) : -1;
+    if (lane == 0) {
+      s_info[0] = -1;
+      s_info[3] = work ? (int)(L % n_tiles) : 0;
+      if (work && goff == nullptr) {
+        s_info[0] = 0;
+        s_info[1] = mt * BM;
+        const int64_t rem = dense_M - (int64_t)mt * BM;
+        s_info[2] = rem < BM ? (int)rem : BM;
+      }
+    }
+    if (work && goff != nullptr) {
+      int pre = incl - local;
+      for (int q = 0; q < gpl; ++q) {
+        const int g = g0 + q;
+        if (g >= G) break;
+        const int Mg = goff[g + 1] - goff[g];
+        const int tiles = (Mg + BM - 1) / BM;
+        if (mt >= pre && mt < pre + tiles) {
+          const int r = mt - pre;
+          s_info[0] = g;
+          s_info[1] = goff[g] + r * BM;
+          s_info[2] = (Mg - r * BM) < BM ? (Mg - r * BM) : BM;
+        }
+        pre += tiles;
+      }
+    }
+  }
+  __syncthreads();
+  tl.g = s_info[0];
+  tl.row0 = s_info[1];
+  tl.M = tl.g < 0 ? 0 : s_info[2];
+  tl.nt = s_info[3];
+  if (tl.row0 >= max_rows) tl.M = 0;
+  else if (tl.row0 + tl.M > max_rows) tl.M = (int)(max_rows - tl.row0);
+  return tl;
+}
+
+// Blocks to launch for a tile bound: every XCD band must be coverable.
+static inline int64_t grid_blocks(int64_t bound_m_tiles, int n_tiles) {
+  const int64_t bound = bound_m_tiles * n_tiles;
+  return (bound + 2 * kXcds - 1) / kXcds * kXcds;
+}
+
+}  // namespace moe

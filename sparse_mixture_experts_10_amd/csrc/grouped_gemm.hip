@@ -16,77 +16,19 @@
 // bank-conflict free.  The output tile is staged through LDS so every global
 // store is a full 16-byte vector.
 //
-// Ragged groups: the grid is sized from a host bound on the row count; each
-// block finds its (group, row tile) from the device-side group offsets with a
-// wave-wide prefix scan, and blocks past the last tile exit at once.  The host
-// never reads the per-expert counts.
+// Ragged groups: the 1-D grid is sized from a host bound on the row count;
+// each block finds its (group, row tile, N tile) from the device-side group
+// offsets with a wave-wide prefix scan, and blocks past the last tile exit at
+// once.  The host never reads the per-expert counts.  Tiles are dealt to the
+// 8 XCDs in contiguous bands (see find_tile) for L2 locality.
 
 #include "common.h"
 #include "internal.h"
+#include "gemm_tiles.h"
 
 namespace moe {
 
 namespace {
-
-struct Tile {
-  int g;
-  int64_t row0;
-  int M;  // valid rows in this tile (0: block has no work)
-};
-
-// Wave 0 maps blockIdx.x to (group, row tile); result broadcast through LDS.
-template <int BM>
-__device__ Tile find_tile(const int32_t* __restrict__ goff, int G, int64_t dense_M, int64_t max_rows,
-                          int* s_info) {
-  Tile tl;
-  const int64_t bx = blockIdx.x;
-  if (goff == nullptr) {
-    tl.g = 0;
-    tl.row0 = bx * BM;
-    int64_t rem = dense_M - tl.row0;
-    tl.M = rem <= 0 ? 0 : (rem < BM ? (int)rem : BM);
-  } else {
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const int gpl = (G + 63) / 64;  // groups per lane (<= 4)
-      const int g0 = lane * gpl;
-      int local = 0;
-      for (int q = 0; q < gpl; ++q) {
-        const int g = g0 + q;
-        if (g < G) local += (goff[g + 1] - goff[g] + BM - 1) / BM;
-      }
-      int incl = local;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        int o = __shfl_up(incl, m, 64);
-        if (lane >= m) incl += o;
-      }
-      const int total = __shfl(incl, 63, 64);
-      if (lane == 0 && bx >= total) { s_info[0] = -1; s_info[1] = 0; s_info[2] = 0; }
-      int pre = incl - local;
-      for (int q = 0; q < gpl; ++q) {
-        const int g = g0 + q;
-        if (g >= G) break;
-        const int Mg = goff[g + 1] - goff[g];
-        const int tiles = (Mg + BM - 1) / BM;
-        if (bx >= pre && bx < pre + tiles) {
-          const int mt = (int)(bx - pre);
-          s_info[0] = g;
-          s_info[1] = goff[g] + mt * BM;
-          s_info[2] = (Mg - mt * BM) < BM ? (Mg - mt * BM) : BM;
-        }
-        pre += tiles;
-      }
-    }
-    __syncthreads();
-    tl.g = s_info[0];
-    tl.row0 = s_info[1];
-    tl.M = tl.g < 0 ? 0 : s_info[2];
-  }
-  if (tl.row0 >= max_rows) tl.M = 0;
-  else if (tl.row0 + tl.M > max_rows) tl.M = (int)(max_rows - tl.row0);
-  return tl;
-}
 
 __device__ __forceinline__ float bias_at(const bf16_t* bias, int g, int S, int N, int n) {
   if (bias == nullptr) return 0.f;
@@ -114,10 +56,11 @@ constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64, LDK = BK + 8, LDC = BN + 8;
 template <bool SEG>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDK];
-  __shared__ int s_info[3];
+  __shared__ int s_info[4];
   __shared__ float s_sq[2][BM];
 
-  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, s_info);
+  const int n_tiles = (p.N + BN - 1) / BN;
+  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
   if (tl.M <= 0) return;  // uniform
 
   const int tid = threadIdx.x;
@@ -125,7 +68,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int N = p.N, K = p.K;
-  const int n0 = blockIdx.y * BN;
+  const int n0 = tl.nt * BN;
   const bf16_t* A = (const bf16_t*)p.A;
   const bf16_t* B = (const bf16_t*)p.B;
   const int64_t Bg = SEG ? 0 : (int64_t)tl.g * N * K;
@@ -258,14 +201,31 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
       *(vec16*)(C + (tl.row0 + r) * (int64_t)N + n) = *(const vec16*)(Cs + r * LDC + cv * 8);
   }
   if (want_sq && tid < tl.M)
-    p.sq_part[(tl.row0 + tid) * (int64_t)gridDim.y + blockIdx.y] = s_sq[0][tid] + s_sq[1][tid];
+    p.sq_part[(tl.row0 + tid) * (int64_t)n_tiles + tl.nt] = s_sq[0][tid] + s_sq[1][tid];
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+// Tile width the bf16 path uses for these arguments: large tiles only when
+// they still give every CU about two tiles.
+static int bf16_tile(const GemmArgs& a) {
+  if (!gemm_v2_supported(a)) return 0;
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
-  const int64_t gx = (rows + BM - 1) / BM + (a.group_offset ? a.G : 0);
-  if (gx <= 0) return hipSuccess;
-  const dim3 grid((unsigned)gx, (unsigned)((a.N + BN - 1) / BN));
+  const int64_t big = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 127) / 128);
+  return big >= 1024 ? 256 : 128;   // 256 x 128 tiles, or 128 x 128
+}
+
+int gemm_bf16_n_tiles(const GemmArgs& a) { return (a.N + 127) / 128; }
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+  const int t = bf16_tile(a);
+  if (t) return launch_gemm_bf16_v2(a, t, st);
+  return launch_gemm_bf16_v1(a, st);
+}
+
+hipError_t launch_gemm_bf16_v1(const GemmArgs& a, hipStream_t st) {
+  const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
+  const int64_t mt = (rows + BM - 1) / BM + (a.group_offset ? a.G : 0);
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)grid_blocks(mt, (a.N + BN - 1) / BN));
   if (a.S > 1)
     hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, st, a);
   else
@@ -281,15 +241,16 @@ constexpr int FBM = kGemmF32BM, FBN = kGemmF32BN, FBK = 16;
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   __shared__ float As[FBK][FBM + 4];
   __shared__ float Bs[FBK][FBN + 4];
-  __shared__ int s_info[3];
+  __shared__ int s_info[4];
 
-  const Tile tl = find_tile<FBM>(p.group_offset, p.G, p.dense_M, p.max_rows, s_info);
+  const int n_tiles = (p.N + FBN - 1) / FBN;
+  const Tile tl = find_tile<FBM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
   if (tl.M <= 0) return;
 
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int N = p.N, K = p.K;
-  const int n0 = blockIdx.y * FBN;
+  const int n0 = tl.nt * FBN;
   const float* A = (const float*)p.A;
   const float* B = (const float*)p.B;
   const bool seg = p.S > 1;
@@ -352,16 +313,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
       rs += __shfl_xor(rs, 2, 64);
       rs += __shfl_xor(rs, 4, 64);
       rs += __shfl_xor(rs, 8, 64);
-      if (tx == 0 && r < tl.M) p.sq_part[(tl.row0 + r) * (int64_t)gridDim.y + blockIdx.y] = rs;
+      if (tx == 0 && r < tl.M) p.sq_part[(tl.row0 + r) * (int64_t)n_tiles + tl.nt] = rs;
     }
   }
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
-  const int64_t gx = (rows + FBM - 1) / FBM + (a.group_offset ? a.G : 0);
-  if (gx <= 0) return hipSuccess;
-  const dim3 grid((unsigned)gx, (unsigned)((a.N + FBN - 1) / FBN));
+  const int64_t mt = (rows + FBM - 1) / FBM + (a.group_offset ? a.G : 0);
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)grid_blocks(mt, (a.N + FBN - 1) / FBN));
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -222,3 +222,31 @@ def test_full_size_sampled(name):
     tokens = sorted(set([0, 1, w.T - 1] + rng.choice(w.T, 45, replace=False).tolist()))
     rep = check_layer(inp, o, tokens=tokens)
     say(f"  flips={rep.flips} notes={rep.notes}")
+
+
+def test_graph_replay_matches_eager():
+    """The whole pass captured in one HIP graph: every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    w = SCALED["fine_shared_s"].with_(credit=True)
+    inp, layer, x, o = run(w)
+    ref = {n: getattr(o, n).clone() for n in ("y", "topk_idx", "row", "losses", "mean_credit", "y_disp")}
+    g_out = layer.allocate(w.T)
+    layer.forward(x, g_out)                       # warm the allocator outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x, g_out)
+    for rep in range(4):
+        for n in ("y", "y_disp", "losses"):
+            getattr(g_out, n).zero_()
+        layer.forward(x)                          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, r in ref.items():
+            a = getattr(g_out, n)
+            if n == "y_disp":
+                k = int(o.expert_offset[-1])
+                a, r = a[:k], r[:k]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               r.view(torch.int16) if r.dtype == torch.bfloat16 else r), (rep, n)
