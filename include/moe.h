@@ -92,8 +92,8 @@ int moe_capacity(int64_t cf_num, int64_t cf_den, int32_t k, int64_t T, int32_t E
 /*
  * Device workspace size in bytes needed by operation `op` for these sizes
  * (0 when the operation needs none).  Host-only.  Arguments that an operation
- * does not use are ignored: DISPATCH uses T, E; FFN uses F, max_rows (and the
- * element type does not change the size); STATS uses T, E.
+ * does not use are ignored: ROUTER uses T, d, E (the size assumes bf16 x;
+ * fp32 x needs none); DISPATCH uses T, E; FFN uses F, max_rows; STATS uses T, E.
  */
 int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int32_t F,
                         int64_t max_rows, size_t* bytes);
@@ -112,12 +112,19 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
  *   topk_idx [T, k] int32 out: selected experts ordered by (h + b_sel desc,
  *            index asc); equal scores go to the lower index
  *   topk_gate[T, k] fp32 out: exp(h_e) / sum over the selected of exp(h_e')
- * Products and sums are formed in fp64 (exact products), outputs rounded to
- * fp32 once.  T = 0 is a successful no-op.
+ *   ws       MOE_OP_ROUTER workspace (needed only for bf16 x with E * d too
+ *            large for the on-chip path; moe_workspace_bytes says how much).
+ * Selection precision: small E * d, or fp32 x: products and sums in fp64
+ * (exact products).  Otherwise W_g is split exactly into three bf16 parts and
+ * the logits are a bf16 MFMA GEMM with fp32 accumulation; every token whose
+ * k-th / (k+1)-th score gap is within 5e-5 (relative) is then recomputed in
+ * fp64, so selections agree with a float64 evaluation except on gaps near
+ * float64 rounding.  Logits are rounded to fp32 once.  T = 0 is a no-op.
  */
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
                     const float* b_g, const float* b_sel, int32_t E, int32_t k, float* logits,
-                    float* lse, int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+                    float* lse, int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * Dispatch in token order under capacity `capacity` (>= 0, or -1 = no cap).

@@ -108,15 +108,22 @@ def topk(h: np.ndarray, k: int, b_sel: Optional[np.ndarray] = None) -> np.ndarra
 
 
 def near_tie_gap(h: np.ndarray, k: int, b_sel: Optional[np.ndarray] = None) -> np.ndarray:
-    """Per token, (k-th highest score) - ((k+1)-th highest score); +inf when k = E."""
+    """Per token, the smallest gap between consecutive scores among the k + 1
+    highest (k when k = E; +inf when k = 1 = E).
+
+    Comparator support, not part of the layer: the selected set depends on the
+    k-th vs (k+1)-th gap and the listed order on the gaps inside the top k, so a
+    token is a documented near-tie when any of these is tiny.
+    """
     s = np.asarray(h, np.float64)
     if b_sel is not None:
         s = s + np.asarray(b_sel, np.float64)[None, :]
     E = s.shape[1]
-    if k >= E:
+    m = min(k + 1, E)
+    if m < 2:
         return np.full(s.shape[0], np.inf)
-    srt = -np.sort(-s, axis=1)
-    return srt[:, k - 1] - srt[:, k]
+    srt = -np.sort(-s, axis=1)[:, :m]
+    return (srt[:, :-1] - srt[:, 1:]).min(axis=1)
 
 
 def gates(P: np.ndarray, idx: np.ndarray) -> np.ndarray:

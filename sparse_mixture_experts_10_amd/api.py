@@ -80,12 +80,13 @@ def moe_workspace_bytes(op: int, T: int = 0, d: int = 0, E: int = 1, k: int = 1,
     return out.value
 
 
-def moe_router_topk(x, W_g, b_g, b_sel, k, logits, lse, topk_idx, topk_gate, stream=None):
+def moe_router_topk(x, W_g, b_g, b_sel, k, logits, lse, topk_idx, topk_gate, ws=None, stream=None):
     T, d = x.shape
     E = W_g.shape[0]
+    wp, wn = _ws(ws)
     _check("moe_router_topk", load().moe_router_topk(
         _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(logits), _p(lse), _p(topk_idx),
-        _p(topk_gate), _s(stream)))
+        _p(topk_gate), wp, wn, _s(stream)))
 
 
 def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, row, row_token,

@@ -84,6 +84,9 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   switch (op) {
     case MOE_OP_ROUTER:
+      if (T < 0 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = router_uses_mfma(true, d, E) ? router_mfma_ws_bytes(T, d, E) : 0;
+      return MOE_OK;
     case MOE_OP_COMBINE:
     case MOE_OP_SHARED_FFN:
       *bytes = 0;
@@ -107,7 +110,8 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
 
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
                     const float* b_g, const float* b_sel, int32_t E, int32_t k, float* logits,
-                    float* lse, int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+                    float* lse, int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
   if (T < 0 || d < 1 || d % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
@@ -115,8 +119,12 @@ int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const floa
   if (T == 0) return MOE_OK;
   if (!x || !W_g || !logits || !lse || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(W_g)) return MOE_ERR_INVALID_ARG;
+  if (router_uses_mfma(x_dtype == MOE_BF16, d, E)) {
+    const size_t need = router_mfma_ws_bytes(T, d, E);
+    if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
+  }
   return hip_status(launch_router(x, x_dtype == MOE_BF16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
-                                  topk_idx, topk_gate, stream));
+                                  topk_idx, topk_gate, ws, stream));
 }
 
 int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,

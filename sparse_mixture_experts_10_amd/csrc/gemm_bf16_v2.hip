@@ -86,6 +86,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
   const int n0 = tl.nt * BN;
   const bf16_t* A = (const bf16_t*)p.A;
   const bf16_t* B = (const bf16_t*)p.B;
+  const int rep = p.a_repeat > 1 ? p.a_repeat : 1;
+  const int lda = K / rep;
 
   // ---- this lane's load slots: instruction j = wave + NW i fills slab rows
   // 16 j .. 16 j + 15 (1 KB); lane l fills row 16 j + l / 4, physical chunk l % 4,
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     const int chunk = (lane & 3) ^ swz(row);  // logical chunk stored here
     if (row < BM) {
       const int r = row < tl.M ? row : tl.M - 1;
-      src[i] = A + (tl.row0 + r) * (int64_t)K + chunk * 8;
+      src[i] = A + (tl.row0 + r) * (int64_t)lda + chunk * 8;
     } else {
       const int nr = row - BM;
       const int n = (n0 + nr < N) ? n0 + nr : N - 1;
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     for (int i = 0; i < LPW; ++i) {
       const int row0 = 16 * (wave + NW * i);
       int64_t off = k;
+      if (row0 < BM && rep > 1) off = (k / (32 * rep)) * 32;
       if (SEG && row0 >= BM) {
         const int s = k / p.Kseg;
         off = (int64_t)s * N * p.Kseg + (k - s * p.Kseg);
@@ -192,6 +195,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     bcol[j] = bv;
   }
   const bool want_sq = p.sq_part != nullptr;
+  if (p.out_f32) {
+    // fp32 result straight from the accumulators (each 16 lanes store 64
+    // contiguous bytes of one row)
+    float* Cf = (float*)p.C;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm * C::WM + i * 16 + fc * 4 + r;
+          const int n = n0 + wn * C::WN + j * 16 + fr;
+          float v = acc[i][j][r] + bcol[j];
+          if (p.act >= 0) v = apply_act(p.act, v);
+          if (m < tl.M && n < N) Cf[(tl.row0 + m) * (int64_t)N + n] = v;
+        }
+    return;
+  }
   bf16_t* Cs = (bf16_t*)st0;
   bf16_t* Cg = (bf16_t*)p.C;
   // pass i stages row tile i of every wave row (SR rows: staging row
@@ -255,11 +276,12 @@ static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
 }
 
 bool gemm_v2_supported(const GemmArgs& a) {
-  return a.K % 32 == 0 && (a.S <= 1 || a.Kseg % 32 == 0);
+  return a.K % 32 == 0 && (a.S <= 1 || a.Kseg % 32 == 0) && (a.a_repeat <= 1 || a.K % (32 * a.a_repeat) == 0);
 }
 
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   if (tile == 256) return launch_v2<256, 128, 2, 2, 3, 2>(a, st);
+  if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 2>(a, st);
   return launch_v2<128, 128, 2, 2, 4, 2>(a, st);
 }
 

@@ -208,12 +208,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 // they still give every CU about two tiles.
 static int bf16_tile(const GemmArgs& a) {
   if (!gemm_v2_supported(a)) return 0;
+  if (a.N <= 64) return 64;
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
   const int64_t big = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 127) / 128);
   return big >= 1024 ? 256 : 128;   // 256 x 128 tiles, or 128 x 128
 }
 
-int gemm_bf16_n_tiles(const GemmArgs& a) { return (a.N + 127) / 128; }
+int gemm_bf16_n_tiles(const GemmArgs& a) {
+  return bf16_tile(a) == 64 ? (a.N + 63) / 64 : (a.N + 127) / 128;
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int t = bf16_tile(a);

@@ -17,9 +17,12 @@ constexpr int kGemmBM = 128;          // M tile of the bf16 grouped GEMM
 constexpr int kGemmF32BN = 64;        // N tile of the fp32 grouped GEMM
 constexpr int kGemmF32BM = 64;        // M tile of the fp32 grouped GEMM
 
+// ws: MFMA-path scratch (router_mfma_ws_bytes) when router_uses_mfma(), else unused
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
-                         float* lse, int32_t* idx, float* gate, hipStream_t st);
+                         float* lse, int32_t* idx, float* gate, void* ws, hipStream_t st);
+bool router_uses_mfma(bool xbf16, int d, int E);
+size_t router_mfma_ws_bytes(int64_t T, int d, int E);
 
 // workspace: hist [nchunks*E] int32 then chunk_base [nchunks*E] int32
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t capacity,
@@ -41,6 +44,9 @@ struct GemmArgs {
   void* C;                   // [rows, N]
   int act;                   // activation, or -1 for none
   float* sq_part;            // [max_rows][n_tiles] partial sum of squares, or nullptr
+  int a_repeat;              // > 1: each 32-wide K slab of A serves a_repeat consecutive slabs of B
+                             //      (A is [rows, K / a_repeat]); 0 or 1: plain
+  bool out_f32;              // C is fp32 (no staging; bias and activation still apply)
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);     // picks the path below

@@ -76,13 +76,18 @@ __device__ __forceinline__ void group_argmax(double& s, int& e, double& h) {
 // Per-token epilogue.  The NXE lanes of a token hold its fp64 dot products
 // (router bias not yet added): lane eg holds experts e = eg + NXE j, j < TE.
 // Writes logits, lse, top-k indices and gates for token t (when live).
+// With flag_rel > 0 it returns true (on every lane of the token) when two
+// consecutive scores among the k + 1 highest (k when k = E) are closer than
+// flag_rel * max(1, |score|): the selected set or its listed order could then
+// change within the logits' rounding error.
 template <int TE, int NXE>
-__device__ __forceinline__ void token_epilogue(const double (&acc)[TE], int eg, int64_t t, bool live,
+__device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, int64_t t, bool live,
                                                int E, int k, const float* __restrict__ bg,
                                                const float* __restrict__ bsel,
                                                float* __restrict__ logits, float* __restrict__ lse_out,
                                                int32_t* __restrict__ topk_idx,
-                                               float* __restrict__ topk_gate) {
+                                               float* __restrict__ topk_gate,
+                                               double flag_rel = 0.0) {
   const double NEG = -__builtin_huge_val();
   double h[TE], s[TE];
   double m = NEG;
@@ -110,9 +115,12 @@ __device__ __forceinline__ void token_epilogue(const double (&acc)[TE], int eg, 
   // two passes of k argmax rounds: the first sums the selected exp(h - m),
   // the second writes indices and gates in selection order
   float gsum = 0.f;
+  bool near = false;
+  double prev = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
     uint32_t taken = 0;
-    for (int r = 0; r < k; ++r) {
+    const int rounds = (pass == 0 && flag_rel > 0.0 && k < E) ? k + 1 : k;
+    for (int r = 0; r < rounds; ++r) {
       double bs = NEG, bh = 0.0;
       int be = 0x7fffffff;
 #pragma unroll
@@ -122,6 +130,11 @@ __device__ __forceinline__ void token_epilogue(const double (&acc)[TE], int eg, 
         if (ok && (s[j] > bs || (s[j] == bs && e < be))) { bs = s[j]; be = e; bh = h[j]; }
       }
       group_argmax<NXE>(bs, be, bh);
+      if (pass == 0 && flag_rel > 0.0) {
+        if (r > 0 && prev - bs < flag_rel * fmax(1.0, fabs(prev))) near = true;
+        prev = bs;
+      }
+      if (r == k) break;  // the (k+1)-th score only feeds the flag
       if (be % NXE == eg) taken |= 1u << (be / NXE);
       const float ex = expf((float)(bh - m));
       if (pass == 0) {
@@ -132,6 +145,7 @@ __device__ __forceinline__ void token_epilogue(const double (&acc)[TE], int eg, 
       }
     }
   }
+  return near;
 }
 
 template <int EP, bool XBF16>
@@ -349,6 +363,171 @@ static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path for bf16 x and large E * d
+//
+// W_g is split exactly into three bf16 parts, W = hi + mid + lo (truncations:
+// hi keeps the top 8 significand bits, mid the next 8, lo the rest, which fits
+// because fp32 has 24).  Every product x * part is exact in fp32, so a bf16
+// MFMA GEMM of x against the stacked parts [hi; mid; lo] (N = 3E, K = d, fp32
+// accumulation) gives three fp32 partial logits per (token, expert); the
+// finish kernel adds them and the router bias in fp64.  The fp32
+// accumulations are the only rounding; every token with two consecutive top
+// scores within kRefineRel of each other is recomputed exactly in fp64.
+// ---------------------------------------------------------------------------
+constexpr double kRefineRel = 5e-5;
+
+__global__ void router_split_kernel(const float* __restrict__ Wg, int E, int d,
+                                    bf16_t* __restrict__ Ws, int32_t* __restrict__ count) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *count = 0;  // refine list, filled later on this stream
+  const int64_t n = (int64_t)E * d;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float w = Wg[i];
+    const float hi = __uint_as_float(__float_as_uint(w) & 0xffff0000u);
+    const float r1 = w - hi;  // exact: the low 16 significand bits of w
+    const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    const float lo = r1 - mid;  // exact, at most 8 significand bits
+    Ws[i] = (bf16_t)(__float_as_uint(hi) >> 16);
+    Ws[n + i] = (bf16_t)(__float_as_uint(mid) >> 16);
+    Ws[2 * n + i] = (bf16_t)(__float_as_uint(lo) >> 16);
+  }
+}
+
+// Per token: logits = hi + mid + lo partials (fp64) + b_g, softmax / top-k /
+// gates, near-tie flag.  NXE lanes per token, as in the other layouts.
+// Flagged tokens are appended to `list` (their order there is arbitrary; each
+// is recomputed on its own, so results do not depend on it).
+template <int EP>
+__global__ __launch_bounds__(256) void router_finish_kernel(
+    const float* __restrict__ part, int64_t T, int E, int k, const float* __restrict__ bg,
+    const float* __restrict__ bsel, float* __restrict__ logits, float* __restrict__ lse_out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ count,
+    int32_t* __restrict__ list) {
+  constexpr int NXE = (EP >= 256) ? 32 : 16;
+  constexpr int TE = EP / NXE;
+  const int tid = threadIdx.x;
+  const int eg = tid % NXE;
+  const int64_t t = (int64_t)blockIdx.x * (256 / NXE) + tid / NXE;
+  double acc[TE];
+#pragma unroll
+  for (int j = 0; j < TE; ++j) {
+    const int e = eg + NXE * j;
+    double a = 0.0;
+    if (t < T && e < E) {
+      const float* p = part + t * (int64_t)(3 * E) + e;
+      a = (double)p[0] + (double)p[E] + (double)p[2 * E];
+    }
+    acc[j] = a;
+  }
+  const bool near = token_epilogue<TE, NXE>(acc, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
+                                            topk_idx, topk_gate, kRefineRel);
+  if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
+}
+
+// Exact fp64 recomputation of the listed tokens, one token per block at a time.
+// Wave w computes experts w, w + 8, ...: lanes stride the row in float4 chunks
+// (products of bf16 and fp32 are exact in fp64) for two experts at once so
+// plenty of loads are in flight, then wave 0 redoes the epilogue.
+constexpr int kRefineThreads = 512;
+
+template <int EP>
+__global__ __launch_bounds__(kRefineThreads) void router_refine_kernel(
+    const bf16_t* __restrict__ x, int d, const float* __restrict__ Wg, const float* __restrict__ bg,
+    const float* __restrict__ bsel, int E, int k, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ list, float* __restrict__ logits, float* __restrict__ lse_out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+  constexpr int TE = (EP + 63) / 64;
+  constexpr int NWAVE = kRefineThreads / 64;
+  __shared__ double s_h[EP];
+  extern __shared__ float s_x[];  // one token row, fp32
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = *count;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t t = list[i];
+    for (int j = tid; j < d; j += kRefineThreads) s_x[j] = bf16_to_f32(x[t * (int64_t)d + j]);
+    __syncthreads();
+    for (int e0 = wave; e0 < E; e0 += 2 * NWAVE) {
+      const int e1 = e0 + NWAVE;
+      const float4* w0 = (const float4*)(Wg + (int64_t)e0 * d);
+      const float4* w1 = (const float4*)(Wg + (int64_t)(e1 < E ? e1 : e0) * d);
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll 4
+      for (int q = lane; q < d / 4; q += 64) {
+        const float4 u = w0[q], v = w1[q];
+        const float4 xv = ((const float4*)s_x)[q];
+        a0 = fma((double)xv.x, (double)u.x, a0); a0 = fma((double)xv.y, (double)u.y, a0);
+        a0 = fma((double)xv.z, (double)u.z, a0); a0 = fma((double)xv.w, (double)u.w, a0);
+        a1 = fma((double)xv.x, (double)v.x, a1); a1 = fma((double)xv.y, (double)v.y, a1);
+        a1 = fma((double)xv.z, (double)v.z, a1); a1 = fma((double)xv.w, (double)v.w, a1);
+      }
+#pragma unroll
+      for (int m = 32; m > 0; m >>= 1) {
+        a0 += __shfl_xor(a0, m, 64);
+        a1 += __shfl_xor(a1, m, 64);
+      }
+      if (lane == 0) {
+        s_h[e0] = a0;
+        if (e1 < E) s_h[e1] = a1;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      double acc[TE];
+#pragma unroll
+      for (int j = 0; j < TE; ++j) {
+        const int e = lane + 64 * j;
+        acc[j] = e < E ? s_h[e] : 0.0;
+      }
+      token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate);
+    }
+    __syncthreads();
+  }
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+size_t router_mfma_ws_bytes(int64_t T, int d, int E) {
+  return align256((size_t)3 * E * d * sizeof(bf16_t)) + align256((size_t)T * 3 * E * sizeof(float)) +
+         256 + align256((size_t)T * sizeof(int32_t));
+}
+
+bool router_uses_mfma(bool xbf16, int d, int E) {
+  return xbf16 && E > 16 && d % 32 == 0 && !((int64_t)E * d * 4 <= 65536 && E <= 64);
+}
+
+template <int EP>
+static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const float* Wg,
+                                     const float* bg, const float* bsel, int E, int k,
+                                     float* logits, float* lse, int32_t* idx, float* gate,
+                                     void* ws, hipStream_t st) {
+  char* w8 = (char*)ws;
+  bf16_t* Ws = (bf16_t*)w8;
+  w8 += align256((size_t)3 * E * d * sizeof(bf16_t));
+  float* part = (float*)w8;
+  w8 += align256((size_t)T * 3 * E * sizeof(float));
+  int32_t* count = (int32_t*)w8;
+  int32_t* list = (int32_t*)(w8 + 256);
+  const int64_t n = (int64_t)E * d;
+  const int64_t nb = (n + 255) / 256;
+  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, Wg,
+                     E, d, Ws, count);
+  GemmArgs g{};
+  g.A = x; g.group_offset = nullptr; g.G = 1; g.dense_M = T; g.max_rows = T;
+  g.B = Ws; g.N = 3 * E; g.K = d; g.S = 1; g.Kseg = d; g.bias = nullptr; g.C = part;
+  g.act = -1; g.sq_part = nullptr; g.out_f32 = true;
+  hipError_t e = launch_gemm_bf16(g, st);
+  if (e != hipSuccess) return e;
+  constexpr int NXE = (EP >= 256) ? 32 : 16;
+  const int64_t tpb = 256 / NXE;
+  hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
+                     part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list);
+  const unsigned nref = (unsigned)(T < 1024 ? T : 1024);
+  hipLaunchKernelGGL((router_refine_kernel<EP>), dim3(nref), dim3(kRefineThreads), (size_t)d * sizeof(float),
+                     st, (const bf16_t*)x, d, Wg, bg, bsel, E, k, count, list, logits, lse, idx, gate);
+  return hipGetLastError();
+}
+
 template <int EP>
 static hipError_t launch_router_ep(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                    const float* bg, const float* bsel, int E, int k, float* logits,
@@ -366,7 +545,12 @@ static hipError_t launch_router_ep(const void* x, bool xbf16, int64_t T, int d, 
 
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
-                         float* lse, int32_t* idx, float* gate, hipStream_t st) {
+                         float* lse, int32_t* idx, float* gate, void* ws, hipStream_t st) {
+  if (router_uses_mfma(xbf16, d, E)) {
+    if (E <= 64) return launch_router_mfma<64>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
+    if (E <= 128) return launch_router_mfma<128>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
+    return launch_router_mfma<256>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
+  }
   // K-split when W_g fits in 64 KB of LDS and E <= 64
   if ((int64_t)E * d * 4 <= 65536 && E <= 64) {
     if (E <= 8) return launch_router_ksplit<8>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);

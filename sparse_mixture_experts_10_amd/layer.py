@@ -45,6 +45,7 @@ class MoEOutputs:
     losses: torch.Tensor        # [3] = L_aux, L_z, sum
     credit: Optional[torch.Tensor]
     mean_credit: Optional[torch.Tensor]
+    ws_router: torch.Tensor
     ws_dispatch: torch.Tensor
     ws_ffn: Optional[torch.Tensor]
     ws_stats: torch.Tensor
@@ -101,6 +102,7 @@ class MoELayer:
             y=e(T, d), f=e(E, dtype=f32), P=e(E, dtype=f32), losses=e(3, dtype=f32),
             credit=e(T, k, dtype=f32) if self.credit else None,
             mean_credit=e(E, dtype=f32) if self.credit else None,
+            ws_router=_ws(api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E), dev),
             ws_dispatch=_ws(api.moe_workspace_bytes(api.OP_DISPATCH, T=T, E=E), dev),
             ws_ffn=_ws(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dev) if self.credit else None,
             ws_stats=_ws(api.moe_workspace_bytes(api.OP_STATS, T=T, E=E), dev),
@@ -123,7 +125,7 @@ class MoELayer:
     # one method per C-ABI call, in forward order
     def router(self, x, o: MoEOutputs, stream=None) -> None:
         api.moe_router_topk(x, self.W_g, self.b_g, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
-                            o.topk_gate, stream)
+                            o.topk_gate, o.ws_router, stream)
 
     def dispatch(self, x, o: MoEOutputs, stream=None) -> None:
         api.moe_dispatch(o.topk_idx, self.E, o.capacity, x, o.expert_count, o.expert_offset, o.slot,

@@ -66,7 +66,7 @@ def test_capacity_workloads_and_errors():
 
 
 def test_workspace_sizes():
-    assert api.moe_workspace_bytes(api.OP_ROUTER, T=100, E=8) == 0
+    assert api.moe_workspace_bytes(api.OP_ROUTER, T=100, d=8, E=8) == 0
     assert api.moe_workspace_bytes(api.OP_COMBINE) == 0
     d = api.moe_workspace_bytes(api.OP_DISPATCH, T=4096, E=8)
     assert d >= 2 * 64 * 8 * 4 and d % 256 == 0
@@ -83,7 +83,8 @@ def _router(**kw):
     a = dict(x=FAKE, dt=1, T=16, d=8, W=FAKE, bg=NULL, bs=NULL, E=4, k=2, lg=FAKE, lse=FAKE, idx=FAKE, g=FAKE)
     a.update(kw)
     return _native.load().moe_router_topk(a["x"], a["dt"], a["T"], a["d"], a["W"], a["bg"], a["bs"], a["E"],
-                                          a["k"], a["lg"], a["lse"], a["idx"], a["g"], None)
+                                          a["k"], a["lg"], a["lse"], a["idx"], a["g"], a.get("ws"),
+                                          a.get("wsb", 0), None)
 
 
 def test_router_validation():
@@ -100,6 +101,11 @@ def test_router_validation():
     assert _router(x=MIS) == INVALID
     assert _router(T=0) == OK                 # empty batch: nothing to do
     assert _router(T=2**30, k=2) == UNSUPPORTED
+    # bf16 x with a large W_g takes the MFMA path, which needs the workspace
+    assert _router(E=128, d=4096, k=8, ws=None) == WORKSPACE
+    assert _router(E=128, d=4096, k=8, ws=FAKE, wsb=16) == WORKSPACE
+    assert api.moe_workspace_bytes(api.OP_ROUTER, T=32768, d=4096, E=128) >= 3 * 128 * 4096 * 2 + 32768
+    assert api.moe_workspace_bytes(api.OP_ROUTER, T=4096, d=512, E=8) == 0
 
 
 def _dispatch(**kw):

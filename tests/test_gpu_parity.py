@@ -250,3 +250,44 @@ def test_graph_replay_matches_eager():
                 a, r = a[:k], r[:k]
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                r.view(torch.int16) if r.dtype == torch.bfloat16 else r), (rep, n)
+
+
+@pytest.mark.parametrize("E,d,k", [(128, 512, 8), (64, 1024, 6), (40, 2048, 2)])
+def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k):
+    """bf16 x with a large W_g uses the split-W_g MFMA router; tokens near a tie
+    are recomputed in fp64, so the selection equals the float64 oracle's except
+    where the float64 gap itself is at rounding level.  Planted: an exact
+    duplicate row (exact ties: lower index wins), a row one fp32 ulp away
+    (gaps ~1e-7) and a row 1e-6 away."""
+    w = synth.LARGE_CREDIT.with_(T=4096, d=d, F=32, E=E, k=k)
+    inp = synth.draw(w)
+    Wg = inp.W_g.copy()
+    Wg[5] = Wg[3]
+    Wg[7] = np.nextafter(Wg[3], np.float32(np.inf))
+    Wg[9] = (Wg[3].astype(np.float64) + 1e-6 / np.sqrt(d)).astype(np.float32)
+    inp.W_g = Wg
+    say(f"[gpu] router mfma path E={E} d={d} k={k}")
+    from synth.device import to_torch
+    t = to_torch(inp)
+    T = w.T
+    lg = torch.empty(T, E, device="cuda"); lse = torch.empty(T, device="cuda")
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda"); g = torch.empty(T, k, device="cuda")
+    ws = torch.empty(max(api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E), 256), dtype=torch.uint8,
+                     device="cuda")
+    assert api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E) > 0   # the MFMA path is taken
+    api.moe_router_topk(t["x"], t["W_g"], t["b_g"], t["b_sel"], k, lg, lse, idx, g, ws)
+    torch.cuda.synchronize()
+    h = oracle.router_logits(synth.widen(inp.x, "bf16"), Wg, inp.b_g)
+    ref = oracle.topk(h, k, inp.b_sel)
+    gap = oracle.near_tie_gap(h, k, inp.b_sel)
+    got = idx.cpu().numpy()
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    say(f"  tokens with gap<1e-6: {(gap < 1e-6).sum()}, mismatches: {len(bad)}")
+    assert (gap < 1e-6).sum() > 10          # the planted rows do create near-ties
+    for tt in bad:
+        assert gap[tt] < 1e-12, (tt, got[tt], ref[tt], gap[tt])
+    close = lambda a, b, tol: np.abs(a - b) <= tol * np.maximum(1, np.abs(b))
+    assert close(lg.cpu().numpy().astype(np.float64), h, 1e-5).all()
+    P, lse_ref = oracle.softmax_lse(h)
+    assert close(lse.cpu().numpy().astype(np.float64), lse_ref, 1e-5).all()
+    assert close(g.cpu().numpy().astype(np.float64), oracle.gates(P, got.astype(np.int64)), 1e-5).all()

@@ -262,6 +262,17 @@ def test_topk_brute_force(E, data):
         assert tuple(idx[t].tolist()) == oracle.brute_topk(h[t], k)
 
 
+def test_near_tie_gap_hand():
+    """Smallest consecutive gap among the k+1 top scores: scores (5, 1, 3, 3.25, 0),
+    k=2 -> sorted 5, 3.25, 3 -> gaps 1.75, 0.25 -> 0.25; k=1 -> 5 vs 3.25 -> 1.75;
+    k=5=E -> min over all consecutive gaps of 5, 3.25, 3, 1, 0 -> 0.25; E=k=1 -> inf."""
+    h = np.array([[5.0, 1.0, 3.0, 3.25, 0.0]])
+    assert oracle.near_tie_gap(h, 2)[0] == 0.25
+    assert oracle.near_tie_gap(h, 1)[0] == 1.75
+    assert oracle.near_tie_gap(h, 5)[0] == 0.25
+    assert oracle.near_tie_gap(np.array([[2.0]]), 1)[0] == np.inf
+
+
 def test_topk_selection_bias_separation():
     """[Appendix C, Balancing] b_i changes only the selection: gates are unchanged by a
     b_sel that keeps T_k; b_sel = 0 equals no bias; a large b_sel changes the set but
