@@ -44,6 +44,8 @@ def _parse():
     ap.add_argument("--workload", default="default", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--materialise", action="store_true",
+                    help="dispatch writes the packed token rows (x_disp) instead of index-only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -105,7 +107,7 @@ def main():
     shared = (t["sW1"], t["sb1"], t["sW2"], t["sb2"]) if w.n_shared else None
     layer = MoELayer(t["W_g"], t["W1"], t["b1"], t["W2"], t["b2"], k=w.k, act=w.act,
                      capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
-                     alpha=w.alpha, beta=w.beta, credit=w.credit)
+                     alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=not args.materialise)
     x = t["x"]
     o = layer.allocate(w.T)
     calls = [("router", lambda: layer.router(x, o)), ("dispatch", lambda: layer.dispatch(x, o)),
@@ -167,7 +169,9 @@ def main():
     gemm_us = 0.5 * (per_call["expert_up"] + per_call["expert_down"])
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     router_bytes = T * d * eb + E * d * 4 + T * E * 4 + T * 4 + 2 * T * k * 4
-    dispatch_bytes = T * d * eb + rows * d * eb + T * k * 4 * 3 + rows * 4
+    # index-only dispatch: read top-k indices, write slot, row and row_token
+    # (materialised: plus one read of each kept token row and one write of it)
+    dispatch_bytes = T * k * 4 * 3 + rows * 4 + (T * d * eb + rows * d * eb if args.materialise else 0)
     combine_bytes = rows * d * eb + T * d * eb + 2 * T * k * 4 + (T * d * eb if w.n_shared else 0)
 
     def gbps(b, us):

@@ -154,11 +154,15 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
 
 /*
  * Grouped expert FFN over packed rows: for every group g and every row r in
- * group_offset[g] .. group_offset[g+1]-1
- *   hidden[r] = act(W1[g] a[r] + b1[g]),   out[r] = W2[g] hidden[r] + b2[g]
+ * group_offset[g] .. group_offset[g+1]-1, with A(r) = a[r] (a_rows == NULL) or
+ * A(r) = a[a_rows[r]] (rows gathered on the fly, e.g. a = x, a_rows = row_token
+ * from an index-only moe_dispatch):
+ *   hidden[r] = act(W1[g] A(r) + b1[g]),   out[r] = W2[g] hidden[r] + b2[g]
  * ("Code Walkthrough -- SER", The gating / routing path: each expert runs its
  * two-layer MLP w1/b1 -> activation -> w2/b2.)
- *   a            [max_rows, d] device (dtype), e.g. x_disp
+ *   a            [max_rows, d] device (dtype), or any [n, d] when a_rows != NULL
+ *   a_rows       [max_rows] int32 device or NULL: source row of each packed row;
+ *                entries below group_offset[G] must lie in [0, n)
  *   group_offset [G+1] int32 device, non-decreasing, group_offset[0] = 0
  *   max_rows     host upper bound on group_offset[G]; rows at or past max_rows
  *                are neither read nor written
@@ -171,10 +175,11 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
  *   ws           MOE_OP_FFN workspace (used only when hidden_sqnorm != NULL).
  * max_rows = 0 is a successful no-op.
  */
-int moe_grouped_ffn(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
-                    int32_t d, int32_t F, int32_t d_out, int dtype, int act, const void* W1,
-                    const void* b1, const void* W2, const void* b2, void* hidden, void* out,
-                    float* hidden_sqnorm, void* ws, size_t ws_bytes, hipStream_t stream);
+int moe_grouped_ffn(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                    int64_t max_rows, int32_t d, int32_t F, int32_t d_out, int dtype, int act,
+                    const void* W1, const void* b1, const void* W2, const void* b2, void* hidden,
+                    void* out, float* hidden_sqnorm, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * The two passes of moe_grouped_ffn as separate calls (same kernels, same
@@ -184,9 +189,9 @@ int moe_grouped_ffn(const void* a, const int32_t* group_offset, int32_t G, int64
  * Arguments as in moe_grouped_ffn; moe_expert_up takes the MOE_OP_FFN
  * workspace when hidden_sqnorm != NULL.  max_rows = 0 is a successful no-op.
  */
-int moe_expert_up(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
-                  int32_t d, int32_t F, int dtype, int act, const void* W1, const void* b1,
-                  void* hidden, float* hidden_sqnorm, void* ws, size_t ws_bytes,
+int moe_expert_up(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                  int64_t max_rows, int32_t d, int32_t F, int dtype, int act, const void* W1,
+                  const void* b1, void* hidden, float* hidden_sqnorm, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
 int moe_expert_down(const void* hidden, const int32_t* group_offset, int32_t G, int64_t max_rows,

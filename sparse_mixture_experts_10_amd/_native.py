@@ -26,9 +26,10 @@ SIGNATURES = {
                                _P]),
     "moe_dispatch": (_INT, [_P, _I64, _I32, _I32, _I64, _P, _INT, _I32, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
-    "moe_grouped_ffn": (_INT, [_P, _P, _I32, _I64, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P,
-                               _P, _P, _P, _SZ, _P]),
-    "moe_expert_up": (_INT, [_P, _P, _I32, _I64, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_ffn": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P,
+                               _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_up": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P, _SZ,
+                             _P]),
     "moe_expert_down": (_INT, [_P, _P, _I32, _I64, _I32, _I32, _INT, _P, _P, _P, _P]),
     "moe_shared_ffn": (_INT, [_P, _I64, _I32, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P, _P,
                               _P]),

@@ -93,7 +93,7 @@ def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, ro
                  x_disp, ws, stream=None):
     T, k = topk_idx.shape
     d = x.shape[1] if x is not None else 0
-    dt = _dt(x) if x is not None else MOE_BF16
+    dt = _dt(x) if x is not None else MOE_BF16   # index-only dispatch: x and x_disp both None
     wp, wn = _ws(ws)
     _check("moe_dispatch", load().moe_dispatch(
         _p(topk_idx), T, k, E, capacity, _p(x), dt, d, _p(expert_count), _p(expert_offset),
@@ -101,22 +101,24 @@ def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, ro
 
 
 def moe_grouped_ffn(a, group_offset, max_rows, W1, b1, W2, b2, act, hidden, out,
-                    hidden_sqnorm=None, ws=None, stream=None):
+                    hidden_sqnorm=None, ws=None, a_rows=None, stream=None):
     G, F, d = W1.shape
     d_out = W2.shape[1]
     wp, wn = _ws(ws)
     _check("moe_grouped_ffn", load().moe_grouped_ffn(
-        _p(a), _p(group_offset), G, max_rows, d, F, d_out, _dt(a), ACT[act] if isinstance(act, str) else act,
-        _p(W1), _p(b1), _p(W2), _p(b2), _p(hidden), _p(out), _p(hidden_sqnorm), wp, wn, _s(stream)))
+        _p(a), _p(a_rows), _p(group_offset), G, max_rows, d, F, d_out, _dt(a),
+        ACT[act] if isinstance(act, str) else act, _p(W1), _p(b1), _p(W2), _p(b2), _p(hidden), _p(out),
+        _p(hidden_sqnorm), wp, wn, _s(stream)))
 
 
 def moe_expert_up(a, group_offset, max_rows, W1, b1, act, hidden, hidden_sqnorm=None, ws=None,
-                  stream=None):
+                  a_rows=None, stream=None):
     G, F, d = W1.shape
     wp, wn = _ws(ws)
     _check("moe_expert_up", load().moe_expert_up(
-        _p(a), _p(group_offset), G, max_rows, d, F, _dt(a), ACT[act] if isinstance(act, str) else act,
-        _p(W1), _p(b1), _p(hidden), _p(hidden_sqnorm), wp, wn, _s(stream)))
+        _p(a), _p(a_rows), _p(group_offset), G, max_rows, d, F, _dt(a),
+        ACT[act] if isinstance(act, str) else act, _p(W1), _p(b1), _p(hidden), _p(hidden_sqnorm), wp, wn,
+        _s(stream)))
 
 
 def moe_expert_down(hidden, group_offset, max_rows, W2, b2, out, stream=None):

@@ -160,7 +160,8 @@ static int check_ffn_common(int32_t G, int64_t max_rows, int dtype) {
   return MOE_OK;
 }
 
-static int check_up(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
+static int check_up(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                    int64_t max_rows,
                     int32_t d, int32_t F, int dtype, int act, const void* W1, const void* b1,
                     void* hidden, float* hidden_sqnorm, void* ws, size_t ws_bytes) {
   if (int rc = check_ffn_common(G, max_rows, dtype)) return rc;
@@ -187,12 +188,13 @@ static int check_down(const void* hidden, const int32_t* group_offset, int32_t G
   return MOE_OK;
 }
 
-static hipError_t run_up(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
-                         int32_t d, int32_t F, int dtype, int act, const void* W1, const void* b1,
-                         void* hidden, float* hidden_sqnorm, void* ws, hipStream_t stream) {
+static hipError_t run_up(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                         int64_t max_rows, int32_t d, int32_t F, int dtype, int act, const void* W1,
+                         const void* b1, void* hidden, float* hidden_sqnorm, void* ws,
+                         hipStream_t stream) {
   const bool bf16 = dtype == MOE_BF16;
   GemmArgs g{};
-  g.A = a; g.group_offset = group_offset; g.G = G; g.dense_M = 0; g.max_rows = max_rows;
+  g.A = a; g.a_rows = a_rows; g.group_offset = group_offset; g.G = G; g.dense_M = 0; g.max_rows = max_rows;
   g.B = W1; g.N = F; g.K = d; g.S = 1; g.Kseg = d; g.bias = b1; g.C = hidden;
   g.act = act; g.sq_part = hidden_sqnorm ? (float*)ws : nullptr;
   hipError_t e = bf16 ? launch_gemm_bf16(g, stream) : launch_gemm_f32(g, stream);
@@ -211,15 +213,15 @@ static hipError_t run_down(const void* hidden, const int32_t* group_offset, int3
   return dtype == MOE_BF16 ? launch_gemm_bf16(g, stream) : launch_gemm_f32(g, stream);
 }
 
-int moe_expert_up(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
-                  int32_t d, int32_t F, int dtype, int act, const void* W1, const void* b1,
-                  void* hidden, float* hidden_sqnorm, void* ws, size_t ws_bytes,
+int moe_expert_up(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                  int64_t max_rows, int32_t d, int32_t F, int dtype, int act, const void* W1,
+                  const void* b1, void* hidden, float* hidden_sqnorm, void* ws, size_t ws_bytes,
                   hipStream_t stream) {
-  if (int rc = check_up(a, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
+  if (int rc = check_up(a, a_rows, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
                         hidden_sqnorm, ws, ws_bytes))
     return rc;
   if (max_rows == 0) return MOE_OK;
-  return hip_status(run_up(a, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
+  return hip_status(run_up(a, a_rows, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
                            hidden_sqnorm, ws, stream));
 }
 
@@ -231,16 +233,17 @@ int moe_expert_down(const void* hidden, const int32_t* group_offset, int32_t G, 
   return hip_status(run_down(hidden, group_offset, G, max_rows, F, d_out, dtype, W2, b2, out, stream));
 }
 
-int moe_grouped_ffn(const void* a, const int32_t* group_offset, int32_t G, int64_t max_rows,
-                    int32_t d, int32_t F, int32_t d_out, int dtype, int act, const void* W1,
-                    const void* b1, const void* W2, const void* b2, void* hidden, void* out,
-                    float* hidden_sqnorm, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (int rc = check_up(a, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
+int moe_grouped_ffn(const void* a, const int32_t* a_rows, const int32_t* group_offset, int32_t G,
+                    int64_t max_rows, int32_t d, int32_t F, int32_t d_out, int dtype, int act,
+                    const void* W1, const void* b1, const void* W2, const void* b2, void* hidden,
+                    void* out, float* hidden_sqnorm, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (int rc = check_up(a, a_rows, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
                         hidden_sqnorm, ws, ws_bytes))
     return rc;
   if (int rc = check_down(hidden, group_offset, G, max_rows, F, d_out, dtype, W2, b2, out)) return rc;
   if (max_rows == 0) return MOE_OK;
-  hipError_t e = run_up(a, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
+  hipError_t e = run_up(a, a_rows, group_offset, G, max_rows, d, F, dtype, act, W1, b1, hidden,
                         hidden_sqnorm, ws, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(run_down(hidden, group_offset, G, max_rows, F, d_out, dtype, W2, b2, out, stream));

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     const int chunk = (lane & 3) ^ swz(row);  // logical chunk stored here
     if (row < BM) {
       const int r = row < tl.M ? row : tl.M - 1;
-      src[i] = A + (tl.row0 + r) * (int64_t)lda + chunk * 8;
+      const int64_t arow = p.a_rows ? (int64_t)p.a_rows[tl.row0 + r] : tl.row0 + r;
+      src[i] = A + arow * lda + chunk * 8;
     } else {
       const int nr = row - BM;
       const int n = (n0 + nr < N) ? n0 + nr : N - 1;

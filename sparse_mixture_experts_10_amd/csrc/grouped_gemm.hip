@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
     l_row[i] = v >> 3;
     l_cv[i] = v & 7;
     const int ar = l_row[i] < tl.M ? l_row[i] : tl.M - 1;
-    a_off[i] = (tl.row0 + ar) * (int64_t)K;
+    const int64_t arow = p.a_rows ? (int64_t)p.a_rows[tl.row0 + ar] : tl.row0 + ar;
+    a_off[i] = arow * (int64_t)K;
     const int bn = (n0 + l_row[i] < N) ? n0 + l_row[i] : N - 1;
     b_off[i] = SEG ? (int64_t)bn * p.Kseg : Bg + (int64_t)bn * K;
   }
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 
   const int lr = tid >> 2, lc = (tid & 3) * 4;
   const int ar = lr < tl.M ? lr : tl.M - 1;
-  const float* arow = A + (tl.row0 + ar) * (int64_t)K;
+  const float* arow = A + (p.a_rows ? (int64_t)p.a_rows[tl.row0 + ar] : tl.row0 + ar) * (int64_t)K;
   const int bn = (n0 + lr < N) ? n0 + lr : N - 1;
 
   float acc[4][4] = {};

@@ -32,7 +32,8 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
 
 // One grouped GEMM pass  C[r, n] = epi( sum_k A[r, k] * B[g(r)][n, k] ).
 struct GemmArgs {
-  const void* A;             // [rows, K]
+  const void* A;             // [rows, K], or [*, K] read through a_rows
+  const int32_t* a_rows;     // nullptr, or: packed row r reads A row a_rows[r]
   const int32_t* group_offset;  // [G+1] device, or nullptr: one group of dense_M rows
   int G;
   int64_t dense_M;

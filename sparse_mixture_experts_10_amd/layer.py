@@ -33,7 +33,7 @@ class MoEOutputs:
     slot: torch.Tensor          # [T, k] int32
     row: torch.Tensor           # [T, k] int32
     row_token: torch.Tensor     # [rows] int32
-    x_disp: torch.Tensor        # [rows, d]
+    x_disp: Optional[torch.Tensor]  # [rows, d]; None when rows are gathered in the up pass
     hidden: torch.Tensor        # [rows, F]
     y_disp: torch.Tensor        # [rows, d]
     sqnorm: Optional[torch.Tensor]
@@ -49,6 +49,7 @@ class MoEOutputs:
     ws_dispatch: torch.Tensor
     ws_ffn: Optional[torch.Tensor]
     ws_stats: torch.Tensor
+    x: Optional[torch.Tensor] = None  # input of the last dispatch (rows gathered from it)
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:
@@ -62,17 +63,21 @@ class MoELayer:
     W2 [E, d, F], b2 [E, d] in the layer dtype (bf16 or fp32); shared =
     (W1 [S, F, d], b1 [S, F], W2 [S, d, F], b2 [S, d]) or None.
     capacity_factor: a Fraction (or anything Fraction accepts), None = no cap.
+    gather_rows: True (default) dispatches indices only and the expert-up pass
+    reads token rows of x through row_token; False materialises x_disp first.
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
-                 alpha: float = 0.01, beta: float = 1e-3, credit: bool = False):
+                 alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
+                 gather_rows: bool = True):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
         self.k, self.act = k, act
         self.cf = None if capacity_factor is None else Fraction(capacity_factor)
         self.alpha, self.beta, self.credit = alpha, beta, credit
+        self.gather_rows = gather_rows
         self.E, self.F, self.d = W1.shape
         self.dtype = W1.dtype
         self.device = W1.device
@@ -96,7 +101,7 @@ class MoELayer:
             topk_idx=e(T, k, dtype=i32), topk_gate=e(T, k, dtype=f32),
             expert_count=e(E, dtype=i32), expert_offset=e(E + 1, dtype=i32),
             slot=e(T, k, dtype=i32), row=e(T, k, dtype=i32), row_token=e(rows, dtype=i32),
-            x_disp=e(rows, d), hidden=e(rows, F), y_disp=e(rows, d),
+            x_disp=None if self.gather_rows else e(rows, d), hidden=e(rows, F), y_disp=e(rows, d),
             sqnorm=e(rows, dtype=f32) if self.credit else None,
             shared_hidden=e(T, S * F) if S else None, shared_out=e(T, d) if S else None,
             y=e(T, d), f=e(E, dtype=f32), P=e(E, dtype=f32), losses=e(3, dtype=f32),
@@ -128,13 +133,18 @@ class MoELayer:
                             o.topk_gate, o.ws_router, stream)
 
     def dispatch(self, x, o: MoEOutputs, stream=None) -> None:
-        api.moe_dispatch(o.topk_idx, self.E, o.capacity, x, o.expert_count, o.expert_offset, o.slot,
-                         o.row, o.row_token, o.x_disp, o.ws_dispatch, stream)
+        o.x = x
+        api.moe_dispatch(o.topk_idx, self.E, o.capacity, None if self.gather_rows else x, o.expert_count,
+                         o.expert_offset, o.slot, o.row, o.row_token, o.x_disp, o.ws_dispatch, stream)
 
     def expert_up(self, o: MoEOutputs, stream=None) -> None:
         if o.max_rows > 0:
-            api.moe_expert_up(o.x_disp, o.expert_offset, o.max_rows, self.W1, self.b1, self.act, o.hidden,
-                              o.sqnorm, o.ws_ffn, stream)
+            if self.gather_rows:
+                api.moe_expert_up(o.x, o.expert_offset, o.max_rows, self.W1, self.b1, self.act, o.hidden,
+                                  o.sqnorm, o.ws_ffn, a_rows=o.row_token, stream=stream)
+            else:
+                api.moe_expert_up(o.x_disp, o.expert_offset, o.max_rows, self.W1, self.b1, self.act,
+                                  o.hidden, o.sqnorm, o.ws_ffn, stream=stream)
 
     def expert_down(self, o: MoEOutputs, stream=None) -> None:
         if o.max_rows > 0:

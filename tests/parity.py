@@ -38,13 +38,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def build_layer(inp: synth.Inputs, device="cuda"):
+def build_layer(inp: synth.Inputs, device="cuda", gather_rows=True):
     w = inp.workload
     t = to_torch(inp, device)
     shared = (t["sW1"], t["sb1"], t["sW2"], t["sb2"]) if w.n_shared else None
     layer = MoELayer(t["W_g"], t["W1"], t["b1"], t["W2"], t["b2"], k=w.k, act=w.act,
                      capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
-                     alpha=w.alpha, beta=w.beta, credit=w.credit)
+                     alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=gather_rows)
     return layer, t["x"]
 
 
@@ -113,7 +113,7 @@ def check_layer(inp: synth.Inputs, o, tokens: Optional[Sequence[int]] = None) ->
     assert (o.row.cpu().numpy() == d.row).all(), "row"
     nrows = int(d.offset[-1])
     assert (o.row_token[:nrows].cpu().numpy() == d.row_token).all(), "row_token"
-    if nrows:
+    if nrows and o.x_disp is not None:
         ity = np.int16 if inp.x.dtype == np.uint16 else np.int32
         got = o.x_disp[:nrows].cpu().view(torch.int16 if ity == np.int16 else torch.int32).numpy()
         assert (got == inp.x.view(ity)[d.row_token]).all(), "x_disp rows"

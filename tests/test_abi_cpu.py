@@ -135,9 +135,9 @@ def _ffn(**kw):
     a = dict(a=FAKE, go=FAKE, G=4, mr=32, d=8, F=16, do=8, dt=1, act=0, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE,
              h=FAKE, o=FAKE, sq=NULL, ws=NULL, wsb=0)
     a.update(kw)
-    return _native.load().moe_grouped_ffn(a["a"], a["go"], a["G"], a["mr"], a["d"], a["F"], a["do"], a["dt"],
-                                          a["act"], a["W1"], a["b1"], a["W2"], a["b2"], a["h"], a["o"],
-                                          a["sq"], a["ws"], a["wsb"], None)
+    return _native.load().moe_grouped_ffn(a["a"], a.get("ar"), a["go"], a["G"], a["mr"], a["d"], a["F"],
+                                          a["do"], a["dt"], a["act"], a["W1"], a["b1"], a["W2"], a["b2"],
+                                          a["h"], a["o"], a["sq"], a["ws"], a["wsb"], None)
 
 
 def test_grouped_ffn_validation():

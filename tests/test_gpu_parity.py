@@ -28,10 +28,11 @@ SCALED = {
 }
 
 
-def run(w, inp=None):
+def run(w, inp=None, gather_rows=True):
     inp = inp or synth.draw(w)
-    say(f"[gpu] {w.name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F} S={w.n_shared} dtype={w.dtype}")
-    layer, x = build_layer(inp)
+    say(f"[gpu] {w.name} T={w.T} d={w.d} E={w.E} k={w.k} F={w.F} S={w.n_shared} dtype={w.dtype} "
+        f"gather={gather_rows}")
+    layer, x = build_layer(inp, gather_rows=gather_rows)
     o = layer.forward(x)
     torch.cuda.synchronize()
     return inp, layer, x, o
@@ -43,6 +44,14 @@ def test_layer_matches_oracle(name):
     inp, layer, x, o = run(w)
     rep = check_layer(inp, o)
     say(f"  flips={rep.flips} notes={rep.notes}")
+
+
+@pytest.mark.parametrize("name", ["default", "ragged", "ragged_fp32"])
+def test_layer_materialised_dispatch_matches_oracle(name):
+    """Same pass with x_disp written by dispatch and read packed by the up pass."""
+    inp, layer, x, o = run(SCALED[name], gather_rows=False)
+    assert o.x_disp is not None
+    check_layer(inp, o)
 
 
 def test_deterministic_bitwise():
@@ -147,28 +156,35 @@ def test_dispatch_from_oracle_topk():
     assert torch.equal(row, row2)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_grouped_ffn_ragged_groups(dtype):
-    """Grouped FFN alone on packed rows with empty, tiny and multi-tile groups."""
+@pytest.mark.parametrize("dtype,d,gather", [("bf16", 96, False), ("f32", 96, False), ("bf16", 96, True),
+                                             ("bf16", 104, True), ("f32", 40, True)])
+def test_grouped_ffn_ragged_groups(dtype, d, gather):
+    """Grouped FFN alone on packed rows with empty, tiny and multi-tile groups.
+    gather: the rows are read through a row map from a smaller source matrix
+    (d = 104 is not a multiple of 32 and takes the register-staged kernel)."""
     rng = np.random.default_rng(7)
-    G, d, F = 9, 96, 136
+    G, F = 9, 136
     sizes = np.array([0, 1, 127, 128, 129, 0, 300, 5, 64])
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     N = int(off[-1])
-    say(f"[gpu] grouped_ffn {dtype} G={G} rows={N} d={d} F={F}")
-    w = synth.DEFAULT.with_(T=N, d=d, F=F, E=G, dtype=dtype, act="swish")
+    n_src = 97 if gather else N
+    say(f"[gpu] grouped_ffn {dtype} G={G} rows={N} d={d} F={F} gather={gather}")
+    w = synth.DEFAULT.with_(T=n_src, d=d, F=F, E=G, dtype=dtype, act="swish")
     inp = synth.draw(w)
     from synth.device import tensor
     a = tensor(inp.x, dtype, "cuda")
+    rows = rng.integers(0, n_src, N).astype(np.int32) if gather else np.arange(N, dtype=np.int32)
+    a_rows = torch.as_tensor(rows).cuda() if gather else None
     W1, b1, W2, b2 = (tensor(getattr(inp, n), dtype, "cuda") for n in ("W1", "b1", "W2", "b2"))
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     hid = torch.empty(N, F, dtype=tdt, device="cuda")
     out = torch.empty(N, d, dtype=tdt, device="cuda")
     sq = torch.empty(N, dtype=torch.float32, device="cuda")
     ws = torch.empty(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=N), dtype=torch.uint8, device="cuda")
-    api.moe_grouped_ffn(a, torch.as_tensor(off).cuda(), N, W1, b1, W2, b2, "swish", hid, out, sq, ws)
+    api.moe_grouped_ffn(a, torch.as_tensor(off).cuda(), N, W1, b1, W2, b2, "swish", hid, out, sq, ws,
+                        a_rows=a_rows)
     torch.cuda.synchronize()
-    x64 = synth.widen(inp.x, dtype)
+    x64 = synth.widen(inp.x, dtype)[rows]
     ref = np.zeros((N, d))
     refsq = np.zeros(N)
     for g in range(G):
