@@ -30,6 +30,11 @@ METRIC = "MoE-layer fwd tokens/sec at 1 MI355X; grouped-FFN MFMA util %; dispatc
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# Sources that decide which grouped-GEMM kernel runs and what it does: HBM byte
+# counters recorded for an older version of them are not reported.
+GEMM_SOURCES = ["gemm_bf16_v2.hip", "gemm_tiles.h", "grouped_gemm.hip", "internal.h", "common.h"]
+COUNTER_PREFIX = "traffic-json: "
+
 WORKLOADS = {
     "tiny": "TINY", "default": "DEFAULT", "switch_zipf": "SWITCH_ZIPF",
     "fine_shared": "FINE_SHARED", "large_credit": "LARGE_CREDIT",
@@ -52,15 +57,44 @@ def _parse():
 
 
 def copy_calibration():
+    """A plain elementwise copy (dst = -src over 1 GiB of fp32, one kernel per
+    launch): it reads and writes exactly 1 GiB, so the HBM byte counters of its
+    launches give the scale factor for the counters of the other kernels."""
     import torch
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    src.fill_(1)
     for _ in range(3):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+    print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n,
+                      "launches": 3}), flush=True)
+
+
+def gemm_source_tag() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per grouped-GEMM launch (FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter's reading for a plain copy) from the committed counter
+    summaries under profiles/, if one was taken on this workload and on the
+    current kernel sources; else None."""
+    import glob
+    tag = gemm_source_tag()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "gemm_bf16_v2_hbm_counters_*.md"))):
+        with open(path) as fh:
+            for ln in fh:
+                if ln.startswith(COUNTER_PREFIX):
+                    rec = json.loads(ln[len(COUNTER_PREFIX):])
+                    if rec["workload"] == workload and rec["source_tag"] == tag:
+                        return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(w, seconds: float):
@@ -167,6 +201,9 @@ def main():
     eb = 2 if w.dtype == "bf16" else 4
     gemm_flops = 2.0 * rows * d * F                       # one launch (up or down)
     gemm_us = 0.5 * (per_call["expert_up"] + per_call["expert_down"])
+    # algorithmic HBM bytes of one launch, averaged over up and down: rows of A,
+    # one expert weight matrix per group, the output rows
+    gemm_bytes = 0.5 * ((rows * d + E * F * d + rows * F) + (rows * F + E * d * F + rows * d)) * eb
     achieved = gemm_flops / (gemm_us * 1e-6) / 1e12
     router_bytes = T * d * eb + E * d * 4 + T * E * 4 + T * 4 + 2 * T * k * 4
     # index-only dispatch: read top-k indices, write slot, row and row_token
@@ -210,7 +247,8 @@ def main():
                    "n_shared": w.n_shared, "kept_rows": rows},
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (expert up + down, 2 launches/step)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": counter_traffic(w.name),
+                     "algorithmic_bytes": gemm_bytes},
         "mfma_util_pct": 100.0 * achieved / PEAK_BF16_TFLOPS,
         "dispatch_GBps": kernels["dispatch"]["GB/s"],
         "kernels": kernels,
