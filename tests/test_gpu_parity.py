@@ -198,6 +198,47 @@ def test_grouped_ffn_ragged_groups(dtype, d, gather):
     np.testing.assert_allclose(f64(sq), refsq, rtol=1e-5)
 
 
+@pytest.mark.parametrize("act", ["swish", None])
+def test_grouped_gemm_repeatable_full_size(act):
+    """The expert-up pass at the fine-grained workload's full shape (64 ragged
+    groups, 49152 rows, d 2048, F 1408), run three times: the outputs agree bit
+    for bit.  Guards the LDS slab ring against reads racing the refill of
+    their stage (such a race corrupts a few scattered 16-byte chunks)."""
+    counts = torch.randint(596, 988, (64,), generator=torch.Generator().manual_seed(5))
+    off = torch.zeros(65, dtype=torch.int32)
+    off[1:] = torch.cumsum(counts, 0)
+    rows, d, F = int(off[-1]), 2048, 1408
+    say(f"[gpu] grouped gemm repeatability rows={rows} d={d} F={F} act={act}")
+    g = torch.Generator(device="cuda").manual_seed(6)
+    a = torch.randn(rows, d, device="cuda", generator=g).to(torch.bfloat16)
+    W1 = (torch.randn(64, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(64, F, device="cuda", generator=g)).to(torch.bfloat16)
+    goff = off.cuda()
+    outs = []
+    for _ in range(3):
+        hid = torch.zeros(rows, F, dtype=torch.bfloat16, device="cuda")
+        if act is None:
+            api.moe_expert_down(a, goff, rows, W1, b1, hid)
+        else:
+            api.moe_expert_up(a, goff, rows, W1, b1, act, hid)
+        outs.append(hid)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    # spot-check the first and last row of every group against a float64 product
+    got, want = [], []
+    for gi in range(64):
+        Wg = W1[gi].double().cpu()
+        bg = b1[gi].double().cpu()
+        for r in (int(off[gi]), int(off[gi + 1]) - 1):
+            z = Wg @ a[r].double().cpu() + bg
+            if act == "swish":
+                z = z * torch.sigmoid(z)
+            want.append(z.numpy())
+            got.append(f64(outs[0][r]))
+    close_out(np.stack(got), np.stack(want), "bf16", "grouped gemm rows")
+
+
 def test_shared_experts_alone():
     """Shared FFN (one FFN of width S F, segmented second layer) vs the oracle's
     expert-by-expert sum."""
