@@ -144,12 +144,7 @@ def main():
                      alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=not args.materialise)
     x = t["x"]
     o = layer.allocate(w.T)
-    calls = [("router", lambda: layer.router(x, o)), ("dispatch", lambda: layer.dispatch(x, o)),
-             ("expert_up", lambda: layer.expert_up(o)), ("expert_down", lambda: layer.expert_down(o)),
-             ("shared", lambda: layer.shared_experts(x, o)), ("combine", lambda: layer.combine(o)),
-             ("stats", lambda: layer.stats(o))]
-    if not w.n_shared:
-        calls = [c for c in calls if c[0] != "shared"]
+    calls = layer.calls(x, o)
 
     def step():
         for _, fn in calls:
@@ -195,6 +190,21 @@ def main():
                 for i, (name, _) in enumerate(calls)}   # microseconds
     ms_step_eager = sum(per_call.values()) / 1e3
 
+    # The dispatch on its own (the index-only moe_dispatch call, which the fused
+    # routing pass contains), timed the same way, for the dispatch GB/s figure.
+    if "dispatch" not in per_call:
+        dev = [(ev(), ev()) for _ in range(K)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 30e-6 * K))
+        for a, b in dev:
+            a.record()
+            layer.dispatch(x, o)
+            b.record()
+        torch.cuda.synchronize()
+        per_call_dispatch = float(np.median([a.elapsed_time(b) for a, b in dev])) * 1e3
+    else:
+        per_call_dispatch = per_call["dispatch"]
+
     # algorithmic work
     T, d, E, k, F = w.T, w.d, w.E, w.k, w.F
     rows = int(o.expert_offset[-1])
@@ -214,16 +224,24 @@ def main():
     def gbps(b, us):
         return b / (us * 1e-6) / 1e9
 
-    kernels = {
-        "router": {"us": per_call["router"], "GB/s": gbps(router_bytes, per_call["router"])},
-        "dispatch": {"us": per_call["dispatch"], "GB/s": gbps(dispatch_bytes, per_call["dispatch"])},
+    stats_bytes = T * E * 4 + T * 4
+    kernels = {}
+    if "route" in per_call:
+        kernels["route"] = {"us": per_call["route"],
+                            "GB/s": gbps(router_bytes + dispatch_bytes + stats_bytes, per_call["route"])}
+    else:
+        kernels["router"] = {"us": per_call["router"], "GB/s": gbps(router_bytes, per_call["router"])}
+    kernels["dispatch"] = {"us": per_call_dispatch, "GB/s": gbps(dispatch_bytes, per_call_dispatch),
+                           "note": "index-only moe_dispatch timed on its own" if "route" in per_call else ""}
+    kernels.update({
         "expert_up": {"us": per_call["expert_up"],
                       "TFLOP/s": gemm_flops / (per_call["expert_up"] * 1e-6) / 1e12},
         "expert_down": {"us": per_call["expert_down"],
                         "TFLOP/s": gemm_flops / (per_call["expert_down"] * 1e-6) / 1e12},
         "combine": {"us": per_call["combine"], "GB/s": gbps(combine_bytes, per_call["combine"])},
-        "stats": {"us": per_call["stats"]},
-    }
+    })
+    if "stats" in per_call:
+        kernels["stats"] = {"us": per_call["stats"]}
     if w.n_shared:
         kernels["shared"] = {"us": per_call["shared"],
                              "TFLOP/s": 4.0 * T * d * F * w.n_shared / (per_call["shared"] * 1e-6) / 1e12}

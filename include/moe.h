@@ -72,6 +72,7 @@ extern "C" {
 #define MOE_OP_COMBINE 3
 #define MOE_OP_STATS 4
 #define MOE_OP_SHARED_FFN 5
+#define MOE_OP_ROUTE 6
 
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);
@@ -93,7 +94,9 @@ int moe_capacity(int64_t cf_num, int64_t cf_den, int32_t k, int64_t T, int32_t E
  * Device workspace size in bytes needed by operation `op` for these sizes
  * (0 when the operation needs none).  Host-only.  Arguments that an operation
  * does not use are ignored: ROUTER uses T, d, E (the size assumes bf16 x;
- * fp32 x needs none); DISPATCH uses T, E; FFN uses F, max_rows; STATS uses T, E.
+ * fp32 x needs none); DISPATCH uses T, E; FFN uses F, max_rows; STATS uses T, E,
+ * k (the size covers credit); ROUTE uses T, d, E (as ROUTER plus DISPATCH plus
+ * the statistics partials).
  */
 int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int32_t F,
                         int64_t max_rows, size_t* bytes);
@@ -151,6 +154,26 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
                  const void* x, int x_dtype, int32_t d, int32_t* expert_count,
                  int32_t* expert_offset, int32_t* slot, int32_t* row, int32_t* row_token,
                  void* x_disp, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The whole routing half of the layer in one call: moe_router_topk, then an
+ * index-only moe_dispatch, then the statistics f, P and losses of
+ * moe_route_stats (without credit), in three kernels.  Outputs are bit-identical
+ * to those three calls.  ("Appendix C -- Acronyms & Symbols", Core MoE symbols,
+ * Balancing, Capacity & communication; "Code Walkthrough -- SER", The gating /
+ * routing path and Load balancing.)
+ *   x, W_g, b_g, b_sel, logits, lse, topk_idx, topk_gate: as moe_router_topk
+ *   capacity, expert_count, expert_offset, slot, row, row_token: as moe_dispatch
+ *   alpha, beta, f, P, losses: as moe_route_stats
+ *   ws   MOE_OP_ROUTE workspace (256-byte aligned).
+ * T = 0 writes zero counts and offsets and nothing else.
+ */
+int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
+              const float* b_g, const float* b_sel, int32_t E, int32_t k, int64_t capacity,
+              float alpha, float beta, float* logits, float* lse, int32_t* topk_idx,
+              float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
+              int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
+              size_t ws_bytes, hipStream_t stream);
 
 /*
  * Grouped expert FFN over packed rows: for every group g and every row r in

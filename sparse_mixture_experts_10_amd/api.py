@@ -16,7 +16,7 @@ from ._native import load
 
 MOE_F32, MOE_BF16 = 0, 1
 ACT = {"relu": 0, "gelu": 1, "swish": 2}
-OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN = range(6)
+OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN, OP_ROUTE = range(7)
 
 
 class MoEError(RuntimeError):
@@ -98,6 +98,17 @@ def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, ro
     _check("moe_dispatch", load().moe_dispatch(
         _p(topk_idx), T, k, E, capacity, _p(x), dt, d, _p(expert_count), _p(expert_offset),
         _p(slot), _p(row), _p(row_token), _p(x_disp), wp, wn, _s(stream)))
+
+
+def moe_route(x, W_g, b_g, b_sel, k, capacity, alpha, beta, logits, lse, topk_idx, topk_gate,
+              expert_count, expert_offset, slot, row, row_token, f, P, losses, ws, stream=None):
+    T, d = x.shape
+    E = W_g.shape[0]
+    wp, wn = _ws(ws)
+    _check("moe_route", load().moe_route(
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, capacity, alpha, beta, _p(logits),
+        _p(lse), _p(topk_idx), _p(topk_gate), _p(expert_count), _p(expert_offset), _p(slot), _p(row),
+        _p(row_token), _p(f), _p(P), _p(losses), wp, wn, _s(stream)))
 
 
 def moe_grouped_ffn(a, group_offset, max_rows, W1, b1, W2, b2, act, hidden, out,

@@ -31,9 +31,32 @@ inline int check_ek(int32_t E, int32_t k) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-size_t dispatch_ws(int64_t T, int32_t E) {
+// dispatch scratch: chunk counts, group counts (and statistics partials)
+size_t dispatch_ws(int64_t T, int32_t E, bool with_stats = false) {
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
-  return 2 * align_up((size_t)nchunks * (size_t)E * sizeof(int32_t));
+  const int64_t ngroups = (T + kStatsTokens - 1) / kStatsTokens;
+  size_t b = align_up((size_t)nchunks * (size_t)E * sizeof(int32_t)) +
+             align_up((size_t)ngroups * (size_t)E * sizeof(int32_t));
+  if (with_stats) b += align_up((size_t)ngroups * (size_t)(E + 1) * sizeof(double));
+  return b;
+}
+
+DispatchWs dispatch_ws_layout(void* ws, int64_t T, int32_t E) {
+  const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
+  const int64_t ngroups = (T + kStatsTokens - 1) / kStatsTokens;
+  char* p = (char*)ws;
+  DispatchWs w;
+  w.hist = (int32_t*)p;
+  p += align_up((size_t)nchunks * (size_t)E * sizeof(int32_t));
+  w.group = (int32_t*)p;
+  p += align_up((size_t)ngroups * (size_t)E * sizeof(int32_t));
+  w.part = (double*)p;
+  return w;
+}
+
+size_t route_ws(int64_t T, int32_t d, int32_t E, bool xbf16) {
+  const size_t r = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
+  return r + dispatch_ws(T, E, true);
 }
 
 size_t ffn_ws(int32_t F, int64_t max_rows) {
@@ -42,9 +65,15 @@ size_t ffn_ws(int32_t F, int64_t max_rows) {
   return align_up((size_t)max_rows * (size_t)tiles * sizeof(float));
 }
 
-size_t stats_ws(int64_t T, int32_t E) {
+// statistics scratch: block partials, then (credit only) one credit value per
+// packed row
+size_t stats_ws_parts(int64_t T, int32_t E) {
   const int64_t nparts = (T + kStatsTokens - 1) / kStatsTokens;
   return align_up((size_t)nparts * (size_t)(E + 1) * sizeof(double));
+}
+
+size_t stats_ws(int64_t T, int32_t E, int32_t k, bool credit) {
+  return stats_ws_parts(T, E) + (credit ? align_up((size_t)T * (size_t)k * sizeof(float)) : 0);
 }
 
 }  // namespace
@@ -101,7 +130,12 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
       return MOE_OK;
     case MOE_OP_STATS:
       if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
-      *bytes = stats_ws(T, E);
+      if (k < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = stats_ws(T, E, k, true);
+      return MOE_OK;
+    case MOE_OP_ROUTE:
+      if (T < 0 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = route_ws(T, d, E, true);
       return MOE_OK;
     default:
       return MOE_ERR_INVALID_ARG;
@@ -144,12 +178,43 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
   const size_t need = dispatch_ws(T, E);
   if (need > 0 && (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0))
     return MOE_ERR_WORKSPACE;
-  const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
-  int32_t* hist = (int32_t*)ws;
-  int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
   return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, x, elem_bytes(x_dtype), d,
-                                    expert_count, expert_offset, slot, row, row_token, x_disp, hist,
-                                    base, stream));
+                                    expert_count, expert_offset, slot, row, row_token, x_disp,
+                                    dispatch_ws_layout(ws, T, E), nullptr, stream));
+}
+
+int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
+              const float* b_g, const float* b_sel, int32_t E, int32_t k, int64_t capacity,
+              float alpha, float beta, float* logits, float* lse, int32_t* topk_idx,
+              float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
+              int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
+              size_t ws_bytes, hipStream_t stream) {
+  if (int rc = check_ek(E, k)) return rc;
+  if (T < 0 || d < 1 || d % 8 != 0 || capacity < -1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!expert_count || !expert_offset) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!x || !W_g || !logits || !lse || !topk_idx || !topk_gate || !slot || !row || !row_token ||
+        !f || !P || !losses)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(W_g)) return MOE_ERR_INVALID_ARG;
+  }
+  const bool xbf16 = x_dtype == MOE_BF16;
+  const size_t need = route_ws(T, d, E, xbf16);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0))
+    return MOE_ERR_WORKSPACE;
+  const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
+  if (T > 0) {
+    const hipError_t e = launch_router(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse, topk_idx,
+                                       topk_gate, ws, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  RouteStats rs{logits, lse, alpha, beta, f, P, losses};
+  return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
+                                    expert_offset, slot, row, row_token, nullptr,
+                                    dispatch_ws_layout((char*)ws + rws, T, E), T > 0 ? &rs : nullptr,
+                                    stream));
 }
 
 static int check_ffn_common(int32_t G, int64_t max_rows, int dtype) {
@@ -301,11 +366,12 @@ int moe_route_stats(const float* logits, const float* lse, const int32_t* topk_i
     return MOE_ERR_INVALID_ARG;
   if ((credit == nullptr) != (mean_credit == nullptr)) return MOE_ERR_INVALID_ARG;
   if (credit && (!hidden_sqnorm || !row || !expert_offset || !row_token)) return MOE_ERR_INVALID_ARG;
-  const size_t need = stats_ws(T, E);
+  const size_t need = stats_ws(T, E, k, credit != nullptr);
   if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
+  float* credit_row = credit ? (float*)((char*)ws + stats_ws_parts(T, E)) : nullptr;
   return hip_status(launch_stats(logits, lse, topk_idx, topk_gate, expert_count, T, E, k, alpha,
                                  beta, f, P, losses, hidden_sqnorm, row, expert_offset, row_token,
-                                 credit, mean_credit, (double*)ws, stream));
+                                 credit, mean_credit, (double*)ws, credit_row, stream));
 }
 
 }  // extern "C"

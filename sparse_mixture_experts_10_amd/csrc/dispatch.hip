@@ -1,4 +1,4 @@
-// Token-order capacity dispatch: histogram -> scan -> rank + gather.
+// Token-order capacity dispatch: count -> rank + gather.
 //
 // Builds the dispatch of page "Appendix C -- Acronyms & Symbols" (Capacity &
 // communication: capacity C = ceil(C_f k T / E), dispatch tensor D scattering
@@ -14,92 +14,157 @@
 // Everything is integer; LDS atomics only combine order-free integer values
 // (counts, bit masks), so the result is bit-identical run to run.
 //
-// Chunks of 64 tokens (one wavefront) are the unit: kernel 1 counts each
-// chunk's choices per expert, kernel 2 (one block) turns the chunk counts into
-// per-chunk bases and the packed offsets, kernel 3 ranks every choice inside
-// its chunk with a per-expert 64-bit token mask and copies the token rows.
+// Chunks of 64 tokens (one wavefront) are the ranking unit; groups of four
+// chunks (256 tokens) the counting unit.  Kernel 1 (one block per group)
+// counts each chunk's choices per expert and the group's totals, and, in the
+// fused routing pass, also the group's routing-statistics partials.  Kernel 2
+// (one block per chunk) rebuilds from those counts the chunk's per-expert
+// arrival bases and the packed offsets (every block redundantly: no grid-wide
+// step), ranks each choice inside its chunk with a per-expert 64-bit token
+// mask, and copies the token rows when the packed copy is wanted.  Block 0
+// also writes the counts and offsets, and the statistics when asked.
 
 #include "common.h"
 #include "internal.h"
+#include "stats_common.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int64_t T,
-                                                           int k, int E, int32_t* __restrict__ hist) {
-  __shared__ int cnt[kMaxExperts];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+constexpr int kGroupChunks = kStatsTokens / kDispatchChunk;  // 4
+
+// One block of 256 threads per group of 256 tokens.  Wave w counts chunk
+// 4 b + w.  hist[c][e], group[b][e]: counts; part[b][E + 1]: statistics
+// partials (when logits != nullptr).
+__global__ __launch_bounds__(256) void dispatch_count_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int k, int E, int32_t* __restrict__ hist,
+    int32_t* __restrict__ group, const float* __restrict__ logits, const float* __restrict__ lse,
+    double* __restrict__ part) {
+  __shared__ int cnt[kGroupChunks][kMaxExperts];
+  __shared__ double s_red[256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kGroupChunks * kMaxExperts; i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kDispatchChunk + lane;
+  const int64_t c = (int64_t)blockIdx.x * kGroupChunks + wave;
+  const int64_t t = c * kDispatchChunk + lane;
   if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[t * k + j]], 1);
+    for (int j = 0; j < k; ++j) atomicAdd(&cnt[wave][idx[t * k + j]], 1);
   __syncthreads();
-  for (int e = lane; e < E; e += 64) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
+  const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
+  for (int e = tid; e < E; e += 256) {
+    int sum = 0;
+    for (int w = 0; w < kGroupChunks; ++w) {
+      const int64_t cc = (int64_t)blockIdx.x * kGroupChunks + w;
+      if (cc < nchunks) hist[cc * E + e] = cnt[w][e];
+      sum += cnt[w][e];
+    }
+    group[(int64_t)blockIdx.x * E + e] = sum;
+  }
+  if (logits != nullptr) {
+    const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
+    const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
+    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
+  }
 }
 
-// One block.  Thread (g, e): expert e, chunk group g (contiguous chunk range).
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
-                                                             int64_t nchunks, int E, int64_t cap,
-                                                             int32_t* __restrict__ base,
-                                                             int32_t* __restrict__ count,
+__global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __restrict__ count,
                                                              int32_t* __restrict__ offset) {
-  __shared__ int64_t part[1024];
-  __shared__ int64_t kept_s[kMaxExperts];
-  const int ngroups = blockDim.x / E;
-  const int tid = threadIdx.x;
-  const int e = tid % E;
-  const int g = tid / E;
-  const bool active = g < ngroups;
-  const int64_t per = (nchunks + ngroups - 1) / ngroups;
-  const int64_t c0 = (int64_t)g * per;
-  const int64_t c1 = (c0 + per < nchunks) ? c0 + per : nchunks;
-
-  int64_t local = 0;
-  if (active)
-    for (int64_t c = c0; c < c1; ++c) local += hist[c * E + e];
-  part[tid] = local;
-  __syncthreads();
-  if (active) {
-    int64_t run = 0;
-    for (int gg = 0; gg < g; ++gg) run += part[gg * E + e];
-    for (int64_t c = c0; c < c1; ++c) {
-      base[c * E + e] = (int32_t)run;
-      run += hist[c * E + e];
-    }
-    if (g == 0) {
-      int64_t tot = 0;
-      for (int gg = 0; gg < ngroups; ++gg) tot += part[gg * E + e];
-      count[e] = (int32_t)tot;
-      kept_s[e] = (cap < 0 || tot < cap) ? tot : cap;
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int ee = 0; ee < E; ++ee) {
-      offset[ee] = (int32_t)run;
-      run += kept_s[ee];
-    }
-    offset[E] = (int32_t)run;
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    if (e < E) count[e] = 0;
+    offset[e] = 0;
   }
 }
 
 // One block per chunk of 64 tokens; wave 0 ranks, all four waves copy rows.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ offset,
-    int32_t* __restrict__ slot, int32_t* __restrict__ row, int32_t* __restrict__ row_token,
-    const vec16* __restrict__ x, int64_t vecs_per_row, vec16* __restrict__ x_disp) {
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int ngroups,
+    int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot,
+    int32_t* __restrict__ row, int32_t* __restrict__ row_token, const vec16* __restrict__ x,
+    int64_t vecs_per_row, vec16* __restrict__ x_disp, const double* __restrict__ part, float alpha,
+    float beta, float* __restrict__ f, float* __restrict__ Pm, float* __restrict__ losses) {
   __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_scan[256];
+  __shared__ int s_red_i[256];
+  __shared__ int s_wsum[4];
   __shared__ int rows_s[kDispatchChunk * kMaxTopK];
+  __shared__ double s_red[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int64_t t = c * kDispatchChunk + lane;
+  const int64_t grp = c / kGroupChunks;
 
-  for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
+  // arrival base of this chunk and totals per expert.  Thread (q, e) sums
+  // groups q, q + Q, ... (Q = 256 / E thread rows); integer sums, so the
+  // split does not change the result.
+  {
+    const int Q = 256 / E;
+    const int e = tid % E, q = tid / E;
+    int pre = 0, tot = 0;
+    if (q < Q) {
+      int b = q;
+      for (; b + 3 * Q < ngroups; b += 4 * Q) {
+        const int v0 = group[(int64_t)b * E + e], v1 = group[(int64_t)(b + Q) * E + e];
+        const int v2 = group[(int64_t)(b + 2 * Q) * E + e], v3 = group[(int64_t)(b + 3 * Q) * E + e];
+        pre += (b < grp ? v0 : 0) + (b + Q < grp ? v1 : 0) + (b + 2 * Q < grp ? v2 : 0) +
+               (b + 3 * Q < grp ? v3 : 0);
+        tot += v0 + v1 + v2 + v3;
+      }
+      for (; b < ngroups; b += Q) {
+        const int v = group[(int64_t)b * E + e];
+        pre += b < grp ? v : 0;
+        tot += v;
+      }
+      if (q == 0)
+        for (int64_t cc = grp * kGroupChunks; cc < c; ++cc) pre += hist[cc * E + e];
+    }
+    s_scan[tid] = pre;
+    s_red_i[tid] = tot;
+  }
   __syncthreads();
+  int kept = 0;
+  if (tid < E) {
+    const int Q = 256 / E;
+    int pre = 0, tot = 0;
+    for (int q = 0; q < Q; ++q) {
+      pre += s_scan[q * E + tid];
+      tot += s_red_i[q * E + tid];
+    }
+    s_base[tid] = pre;
+    s_cnt[tid] = tot;
+    kept = (cap < 0 || tot < cap) ? tot : (int)cap;
+    mask[tid] = 0ull;
+  }
+  __syncthreads();
+  // exclusive scan of kept over the experts: shuffle scan per wave, then
+  // the wave totals
+  {
+    int v = kept;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(v, m, 64);
+      if (lane >= m) v += o;
+    }
+    if (lane == 63) s_wsum[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    v += before;                       // inclusive prefix over all experts <= tid
+    if (tid < E) s_off[tid] = v - kept;
+    if (tid == E - 1) s_off[E] = v;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += 256) count[e] = s_cnt[e];
+    for (int e = tid; e <= E; e += 256) offset[e] = s_off[e];
+    if (f != nullptr) stats_finish(part, ngroups, s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red);
+  }
+
   if (wave == 0 && t < T)
     for (int j = 0; j < k; ++j) atomicOr(&mask[idx[t * k + j]], 1ull << lane);
   __syncthreads();
@@ -109,10 +174,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       int r = -1;
       if (t < T) {
         const int e = idx[t * k + j];
-        const int s = base[c * E + e] + __popcll(mask[e] & below);
+        const int s = s_base[e] + __popcll(mask[e] & below);
         slot[t * k + j] = s;
         if (cap < 0 || s < cap) {
-          r = offset[e] + s;
+          r = s_off[e] + s;
           row_token[r] = (int32_t)t;
         }
         row[t * k + j] = r;
@@ -141,21 +206,24 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t capacity,
                            const void* x, int elem_bytes, int d, int32_t* count,
                            int32_t* offset, int32_t* slot, int32_t* row, int32_t* row_token,
-                           void* x_disp, int32_t* ws_hist, int32_t* ws_base, hipStream_t st) {
+                           void* x_disp, const DispatchWs& ws, const RouteStats* stats,
+                           hipStream_t st) {
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nchunks), dim3(64), 0, st, idx, T, k, E,
-                       ws_hist);
+  const int64_t ngroups = (T + kStatsTokens - 1) / kStatsTokens;
+  if (ngroups == 0) {
+    // no tokens: every expert is empty (and there are no statistics to take)
+    hipLaunchKernelGGL(dispatch_empty_kernel, dim3(1), dim3(256), 0, st, E, count, offset);
+    return hipGetLastError();
   }
-  const int threads = (1024 / E) * E;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(threads), 0, st, ws_hist, nchunks, E,
-                     capacity, ws_base, count, offset);
-  if (nchunks > 0) {
-    const int64_t vpr = (int64_t)d * elem_bytes / 16;
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, idx, T,
-                       k, E, capacity, ws_base, offset, slot, row, row_token, (const vec16*)x, vpr,
-                       (vec16*)x_disp);
-  }
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3((unsigned)ngroups), dim3(256), 0, st, idx, T, k, E,
+                     ws.hist, ws.group, stats ? stats->logits : nullptr, stats ? stats->lse : nullptr,
+                     ws.part);
+  const int64_t vpr = (int64_t)d * elem_bytes / 16;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, idx, T, k, E,
+                     capacity, ws.hist, ws.group, (int)ngroups, count, offset, slot, row, row_token,
+                     (const vec16*)x, vpr, (vec16*)x_disp, ws.part, stats ? stats->alpha : 0.f,
+                     stats ? stats->beta : 0.f, stats ? stats->f : nullptr, stats ? stats->P : nullptr,
+                     stats ? stats->losses : nullptr);
   return hipGetLastError();
 }
 

@@ -24,11 +24,28 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
 bool router_uses_mfma(bool xbf16, int d, int E);
 size_t router_mfma_ws_bytes(int64_t T, int d, int E);
 
-// workspace: hist [nchunks*E] int32 then chunk_base [nchunks*E] int32
+// Dispatch scratch: per-chunk counts [nchunks][E], per-group counts
+// [ngroups][E] (a group is kStatsTokens tokens), and, for the fused routing
+// pass, statistics partials [ngroups][E + 1].
+struct DispatchWs {
+  int32_t* hist;
+  int32_t* group;
+  double* part;
+};
+// Routing statistics taken in the same pass as the dispatch (nullptr: none).
+struct RouteStats {
+  const float* logits;
+  const float* lse;
+  float alpha, beta;
+  float* f;
+  float* P;
+  float* losses;
+};
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t capacity,
                            const void* x, int elem_bytes, int d, int32_t* count,
                            int32_t* offset, int32_t* slot, int32_t* row, int32_t* row_token,
-                           void* x_disp, int32_t* ws_hist, int32_t* ws_base, hipStream_t st);
+                           void* x_disp, const DispatchWs& ws, const RouteStats* stats,
+                           hipStream_t st);
 
 // One grouped GEMM pass  C[r, n] = epi( sum_k A[r, k] * B[g(r)][n, k] ).
 struct GemmArgs {
@@ -63,12 +80,12 @@ hipError_t launch_combine(const void* expert_out, const int32_t* row, const floa
                           const void* shared_out, int64_t T, int k, int d_out, bool bf16,
                           void* y, hipStream_t st);
 
-// workspace: partial [nblocks][E+1] double
+// workspace: partial [nblocks][E+1] double; credit_row [rows] float (credit only)
 hipError_t launch_stats(const float* logits, const float* lse, const int32_t* idx,
                         const float* gate, const int32_t* count, int64_t T, int E, int k,
                         float alpha, float beta, float* f, float* Pm, float* losses,
                         const float* sq, const int32_t* row, const int32_t* offset,
                         const int32_t* row_token, float* credit, float* mean_credit,
-                        double* ws_partial, hipStream_t st);
+                        double* ws_partial, float* credit_row, hipStream_t st);
 
 }  // namespace moe

@@ -13,58 +13,31 @@
 //
 // Deterministic: no floating-point atomics.  Kernel 1 gives every block of 256
 // tokens fixed-order partial sums (fp64) of softmax mass per expert and of
-// lse^2, and writes the per-choice credit.  Kernel 2 sums the partials in
+// lse^2, and writes the per-choice credit (also stored per packed row).  Kernel 2 sums the partials in
 // block order (block 0) and, in blocks 1..E, each expert's credit over its
 // packed rows in row order.
 
 #include "common.h"
 #include "internal.h"
+#include "stats_common.h"
 
 namespace moe {
 
 __global__ __launch_bounds__(256) void stats_partial_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse, int64_t T, int E, int k,
     const float* __restrict__ gate, const float* __restrict__ sq, const int32_t* __restrict__ row,
-    float* __restrict__ credit, double* __restrict__ part) {
+    float* __restrict__ credit, double* __restrict__ part, float* __restrict__ credit_row) {
   __shared__ double s_red[256];
-  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
   const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
-
-  // softmax mass: thread (grp, e) sums tokens t0 + grp, t0 + grp + ngrp, ...
-  const int ngrp = 256 / E;
-  const int e = tid % E, grp = tid / E;
-  double m = 0.0;
-  if (grp < ngrp)
-    for (int64_t t = t0 + grp; t < t1; t += ngrp) m += (double)expf(logits[t * E + e] - lse[t]);
-  s_red[tid] = m;
-  __syncthreads();
-  if (tid < E) {
-    double s = 0.0;
-    for (int q = 0; q < ngrp; ++q) s += s_red[q * E + tid];
-    part[(int64_t)blockIdx.x * (E + 1) + tid] = s;
-  }
-  __syncthreads();
-
-  // lse^2: one token per thread, fixed-order tree over the block
-  const int64_t t = t0 + tid;
-  double z = 0.0;
-  if (t < t1) {
-    const double l = (double)lse[t];
-    z = l * l;
-  }
-  s_red[tid] = z;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] += s_red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) part[(int64_t)blockIdx.x * (E + 1) + E] = s_red[0];
-
+  stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
+  const int64_t t = t0 + threadIdx.x;
   if (credit != nullptr && t < t1) {
     for (int j = 0; j < k; ++j) {
       const int r = row[t * k + j];
-      credit[t * k + j] = r >= 0 ? gate[t * k + j] * sqrtf(sq[r]) : 0.f;
+      const float c = r >= 0 ? gate[t * k + j] * sqrtf(sq[r]) : 0.f;
+      credit[t * k + j] = c;
+      if (r >= 0) credit_row[r] = c;
     }
   }
 }
@@ -73,45 +46,29 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
 __global__ __launch_bounds__(256) void stats_final_kernel(
     const double* __restrict__ part, int nparts, const int32_t* __restrict__ count, int64_t T,
     int E, int k, float alpha, float beta, float* __restrict__ f, float* __restrict__ Pm,
-    float* __restrict__ losses, const int32_t* __restrict__ idx, const float* __restrict__ gate,
-    const float* __restrict__ sq, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ row_token, float* __restrict__ mean_credit) {
+    float* __restrict__ losses, const int32_t* __restrict__ offset,
+    const float* __restrict__ credit_row, float* __restrict__ mean_credit) {
   __shared__ double s_red[256];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
-    if (tid < E) {
-      double s = 0.0;
-      for (int b = 0; b < nparts; ++b) s += part[(int64_t)b * (E + 1) + tid];
-      const double pe = s / (double)T;
-      const double fe = (double)count[tid] / ((double)k * (double)T);
-      Pm[tid] = (float)pe;
-      f[tid] = (float)fe;
-      s_red[tid] = fe * pe;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double fp = 0.0;
-      for (int ee = 0; ee < E; ++ee) fp += s_red[ee];
-      double z = 0.0;
-      for (int b = 0; b < nparts; ++b) z += part[(int64_t)b * (E + 1) + E];
-      const double la = (double)alpha * (double)E * fp;
-      const double lz = (double)beta * z / (double)T;
-      losses[0] = (float)la;
-      losses[1] = (float)lz;
-      losses[2] = (float)(la + lz);
-    }
+    stats_finish(part, nparts, count, T, E, k, alpha, beta, f, Pm, losses, s_red);
     return;
   }
   const int e = blockIdx.x - 1;
   const int64_t r0 = offset[e], r1 = offset[e + 1];
+  // rows of expert e in row order per thread; the credit of each kept row was
+  // stored by the partial kernel
   double s = 0.0;
-  for (int64_t r = r0 + tid; r < r1; r += 256) {
-    const int64_t t = row_token[r];
-    float g = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (idx[t * k + j] == e) g = gate[t * k + j];
-    s += (double)(g * sqrtf(sq[r]));
+  int64_t r = r0 + tid;
+  for (; r + 3 * 256 < r1; r += 4 * 256) {
+    const float c0 = credit_row[r], c1 = credit_row[r + 256], c2 = credit_row[r + 512],
+                c3 = credit_row[r + 768];
+    s += (double)c0;
+    s += (double)c1;
+    s += (double)c2;
+    s += (double)c3;
   }
+  for (; r < r1; r += 256) s += (double)credit_row[r];
   s_red[tid] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -126,14 +83,15 @@ hipError_t launch_stats(const float* logits, const float* lse, const int32_t* id
                         float alpha, float beta, float* f, float* Pm, float* losses,
                         const float* sq, const int32_t* row, const int32_t* offset,
                         const int32_t* row_token, float* credit, float* mean_credit,
-                        double* ws_partial, hipStream_t st) {
+                        double* ws_partial, float* credit_row, hipStream_t st) {
+  (void)idx;
+  (void)row_token;
   const int64_t nparts = (T + kStatsTokens - 1) / kStatsTokens;
   hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)nparts), dim3(256), 0, st, logits, lse, T,
-                     E, k, gate, sq, row, credit, ws_partial);
+                     E, k, gate, sq, row, credit, ws_partial, credit_row);
   const unsigned nblk = mean_credit != nullptr ? (unsigned)(E + 1) : 1u;
   hipLaunchKernelGGL(stats_final_kernel, dim3(nblk), dim3(256), 0, st, ws_partial, (int)nparts, count,
-                     T, E, k, alpha, beta, f, Pm, losses, idx, gate, sq, offset, row_token,
-                     mean_credit);
+                     T, E, k, alpha, beta, f, Pm, losses, offset, credit_row, mean_credit);
   return hipGetLastError();
 }
 

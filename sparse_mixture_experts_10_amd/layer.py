@@ -49,6 +49,7 @@ class MoEOutputs:
     ws_dispatch: torch.Tensor
     ws_ffn: Optional[torch.Tensor]
     ws_stats: torch.Tensor
+    ws_route: Optional[torch.Tensor] = None
     x: Optional[torch.Tensor] = None  # input of the last dispatch (rows gathered from it)
 
 
@@ -65,12 +66,14 @@ class MoELayer:
     capacity_factor: a Fraction (or anything Fraction accepts), None = no cap.
     gather_rows: True (default) dispatches indices only and the expert-up pass
     reads token rows of x through row_token; False materialises x_disp first.
+    fused_route: True (default, with gather_rows) takes router, dispatch and
+    statistics in one moe_route call; False makes the three calls separately.
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
-                 gather_rows: bool = True):
+                 gather_rows: bool = True, fused_route: bool = True):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
@@ -78,6 +81,7 @@ class MoELayer:
         self.cf = None if capacity_factor is None else Fraction(capacity_factor)
         self.alpha, self.beta, self.credit = alpha, beta, credit
         self.gather_rows = gather_rows
+        self.fused = fused_route and gather_rows
         self.E, self.F, self.d = W1.shape
         self.dtype = W1.dtype
         self.device = W1.device
@@ -110,7 +114,8 @@ class MoELayer:
             ws_router=_ws(api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E), dev),
             ws_dispatch=_ws(api.moe_workspace_bytes(api.OP_DISPATCH, T=T, E=E), dev),
             ws_ffn=_ws(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dev) if self.credit else None,
-            ws_stats=_ws(api.moe_workspace_bytes(api.OP_STATS, T=T, E=E), dev),
+            ws_stats=_ws(api.moe_workspace_bytes(api.OP_STATS, T=T, E=E, k=k), dev),
+            ws_route=_ws(api.moe_workspace_bytes(api.OP_ROUTE, T=T, d=d, E=E), dev) if self.fused else None,
         )
 
     def forward(self, x: torch.Tensor, out: Optional[MoEOutputs] = None, stream=None) -> MoEOutputs:
@@ -118,16 +123,34 @@ class MoELayer:
         o = self.allocate(T) if out is None else out
         if o.T != T:
             raise ValueError("output buffers were allocated for another batch size")
-        self.router(x, o, stream)
-        self.dispatch(x, o, stream)
-        self.expert_up(o, stream)
-        self.expert_down(o, stream)
-        self.shared_experts(x, o, stream)
-        self.combine(o, stream)
-        self.stats(o, stream)
+        for _, call in self.calls(x, o, stream):
+            call()
         return o
 
+    def calls(self, x, o: MoEOutputs, stream=None):
+        """The ABI calls of one forward pass, in order, as (name, thunk) pairs."""
+        c = []
+        if self.fused:
+            c.append(("route", lambda: self.route(x, o, stream)))
+        else:
+            c.append(("router", lambda: self.router(x, o, stream)))
+            c.append(("dispatch", lambda: self.dispatch(x, o, stream)))
+        c.append(("expert_up", lambda: self.expert_up(o, stream)))
+        c.append(("expert_down", lambda: self.expert_down(o, stream)))
+        if self.shared is not None:
+            c.append(("shared", lambda: self.shared_experts(x, o, stream)))
+        c.append(("combine", lambda: self.combine(o, stream)))
+        if not self.fused or self.credit:
+            c.append(("stats", lambda: self.stats(o, stream)))
+        return c
+
     # one method per C-ABI call, in forward order
+    def route(self, x, o: MoEOutputs, stream=None) -> None:
+        o.x = x
+        api.moe_route(x, self.W_g, self.b_g, self.b_sel, self.k, o.capacity, self.alpha, self.beta,
+                      o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, o.expert_offset, o.slot,
+                      o.row, o.row_token, o.f, o.P, o.losses, o.ws_route, stream)
+
     def router(self, x, o: MoEOutputs, stream=None) -> None:
         api.moe_router_topk(x, self.W_g, self.b_g, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
                             o.topk_gate, o.ws_router, stream)

@@ -38,13 +38,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def build_layer(inp: synth.Inputs, device="cuda", gather_rows=True):
+def build_layer(inp: synth.Inputs, device="cuda", gather_rows=True, fused_route=True):
     w = inp.workload
     t = to_torch(inp, device)
     shared = (t["sW1"], t["sb1"], t["sW2"], t["sb2"]) if w.n_shared else None
     layer = MoELayer(t["W_g"], t["W1"], t["b1"], t["W2"], t["b2"], k=w.k, act=w.act,
                      capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
-                     alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=gather_rows)
+                     alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=gather_rows,
+                     fused_route=fused_route)
     return layer, t["x"]
 
 

@@ -69,7 +69,7 @@ def test_workspace_sizes():
     assert api.moe_workspace_bytes(api.OP_ROUTER, T=100, d=8, E=8) == 0
     assert api.moe_workspace_bytes(api.OP_COMBINE) == 0
     d = api.moe_workspace_bytes(api.OP_DISPATCH, T=4096, E=8)
-    assert d >= 2 * 64 * 8 * 4 and d % 256 == 0
+    assert d >= 64 * 8 * 4 + 16 * 8 * 4 and d % 256 == 0   # chunk counts, group counts
     assert api.moe_workspace_bytes(api.OP_FFN, F=1536, max_rows=1000) >= 1000 * 24 * 4
     assert api.moe_workspace_bytes(api.OP_STATS, T=1000, E=128) >= 4 * 129 * 8
     lib = _native.load()
@@ -129,6 +129,40 @@ def test_dispatch_validation():
     assert _dispatch(wsb=16) == WORKSPACE
     assert _dispatch(ws=ctypes.c_void_p(0x7f0000000010)) == WORKSPACE   # not 256-byte aligned
     assert _dispatch(slot=NULL) == INVALID
+
+
+def _route(**kw):
+    a = dict(x=FAKE, dt=1, T=16, d=8, W=FAKE, bg=NULL, bs=NULL, E=4, k=2, cap=32, lg=FAKE, lse=FAKE,
+             idx=FAKE, g=FAKE, cnt=FAKE, off=FAKE, slot=FAKE, row=FAKE, rt=FAKE, f=FAKE, P=FAKE, L=FAKE,
+             ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return _native.load().moe_route(a["x"], a["dt"], a["T"], a["d"], a["W"], a["bg"], a["bs"], a["E"], a["k"],
+                                    a["cap"], 0.01, 1e-3, a["lg"], a["lse"], a["idx"], a["g"], a["cnt"],
+                                    a["off"], a["slot"], a["row"], a["rt"], a["f"], a["P"], a["L"], a["ws"],
+                                    a["wsb"], None)
+
+
+def test_route_validation():
+    assert _route(k=0) == INVALID
+    assert _route(k=5) == INVALID
+    assert _route(E=300) == UNSUPPORTED
+    assert _route(cap=-2) == INVALID
+    assert _route(d=12) == INVALID
+    assert _route(dt=5) == UNSUPPORTED
+    assert _route(x=NULL) == INVALID
+    assert _route(f=NULL) == INVALID
+    assert _route(cnt=NULL) == INVALID
+    assert _route(rt=NULL) == INVALID
+    assert _route(x=MIS) == INVALID
+    assert _route(ws=NULL) == WORKSPACE
+    assert _route(wsb=64) == WORKSPACE
+    assert _route(ws=ctypes.c_void_p(0x7f0000000010)) == WORKSPACE
+    assert _route(T=2**30) == UNSUPPORTED
+    # the routing workspace covers the router's and the dispatch's
+    for T, d, E in ((4096, 512, 8), (32768, 4096, 128), (1, 8, 1)):
+        r = api.moe_workspace_bytes(api.OP_ROUTE, T=T, d=d, E=E)
+        assert r >= api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E)
+        assert r >= api.moe_workspace_bytes(api.OP_DISPATCH, T=T, E=E)
 
 
 def _ffn(**kw):

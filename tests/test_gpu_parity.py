@@ -54,6 +54,47 @@ def test_layer_materialised_dispatch_matches_oracle(name):
     check_layer(inp, o)
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged", "switch_zipf_s", "fine_shared_s", "large_credit_s"])
+def test_fused_route_equals_separate_calls(name):
+    """moe_route (router, index-only dispatch and statistics in one call) gives
+    the same bits as moe_router_topk + moe_dispatch + moe_route_stats."""
+    w = SCALED[name]
+    inp = synth.draw(w)
+    say(f"[gpu] fused route vs separate calls: {w.name} T={w.T} E={w.E} k={w.k}")
+    fused, x = build_layer(inp)
+    sep, _ = build_layer(inp, fused_route=False)
+    assert fused.fused and not sep.fused
+    o1, o2 = fused.forward(x), sep.forward(x)
+    torch.cuda.synchronize()
+    n = int(o2.expert_offset[-1])
+    for nm in ("logits", "lse", "topk_idx", "topk_gate", "expert_count", "expert_offset", "slot", "row",
+               "f", "P", "losses", "y"):
+        a, b = getattr(o1, nm), getattr(o2, nm)
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), nm
+    assert torch.equal(o1.row_token[:n], o2.row_token[:n])
+    check_layer(inp, o1)
+
+
+def test_fused_route_empty_batch():
+    """T = 0: counts and offsets are zeroed, nothing else is touched."""
+    E, k, d = 6, 2, 32
+    dev = "cuda"
+    x = torch.empty(0, d, dtype=torch.bfloat16, device=dev)
+    Wg = torch.zeros(E, d, device=dev)
+    cnt = torch.full((E,), 7, dtype=torch.int32, device=dev)
+    off = torch.full((E + 1,), 7, dtype=torch.int32, device=dev)
+    f = torch.full((E,), 3.0, device=dev)
+    e = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    say("[gpu] fused route T=0")
+    api.moe_route(x, Wg, None, None, k, -1, 0.01, 1e-3, e(0, E), e(0), e(0, k, dtype=torch.int32), e(0, k),
+                  cnt, off, e(0, k, dtype=torch.int32), e(0, k, dtype=torch.int32), e(1, dtype=torch.int32),
+                  f, e(E), e(3), ws)
+    torch.cuda.synchronize()
+    assert (cnt == 0).all() and (off == 0).all() and (f == 3.0).all()
+
+
 def test_deterministic_bitwise():
     w = SCALED["large_credit_s"]
     inp, layer, x, o1 = run(w)
