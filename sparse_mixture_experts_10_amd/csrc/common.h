@@ -20,12 +20,11 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.  One
+// v_cvt_pk_bf16_f32 on gfx950 (checked on MI355X against the integer
+// round-to-nearest-even formula over all 2^32 fp32 bit patterns: identical).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const vec16& v, float* f) {
@@ -46,10 +45,32 @@ __device__ __forceinline__ vec16 pack_bf16x8(const float* f) {
 
 enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWISH = 2 };
 
+// GELU(z) = z Phi(z) = 0.5 z (1 + erf(z / sqrt 2)).  erfc(x) for x >= 0 by
+// Abramowitz & Stegun 7.1.26 (t = 1 / (1 + p x), erfc = t (a1 + t (a2 + ...)) e^{-x^2},
+// |error| <= 1.5e-7), with the hardware reciprocal and exp2; then
+// 1 + erf(z / sqrt 2) = 2 - erfc(|z| / sqrt 2) for z >= 0 and erfc(|z| / sqrt 2)
+// for z < 0.  About 15 instructions instead of the library erff's 45.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-1.44269504088896341f * x * x);
+  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+}
+
+// Swish / SiLU z sigmoid(z) = z / (1 + e^{-z}), with the hardware exp2 and
+// reciprocal (each within about 1 ulp).
+__device__ __forceinline__ float swish(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * z));
+}
+
 __device__ __forceinline__ float apply_act(int act, float z) {
   if (act == ACT_RELU) return fmaxf(z, 0.0f);
-  if (act == ACT_GELU) return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-  return z / (1.0f + expf(-z));  // swish / SiLU
+  if (act == ACT_GELU) return gelu_erf(z);
+  return swish(z);
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

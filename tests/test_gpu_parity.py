@@ -280,6 +280,34 @@ def test_grouped_gemm_repeatable_full_size(act):
     close_out(np.stack(got), np.stack(want), "bf16", "grouped gemm rows")
 
 
+@pytest.mark.parametrize("act", ["relu", "gelu", "swish"])
+def test_activation_accuracy(act):
+    """The epilogue activations against their float64 definitions: an fp32 FFN
+    with identity weights returns act(z) itself (each output is one product by
+    1 plus zeros, exact in fp32).  GELU's erf follows Abramowitz & Stegun
+    7.1.26 (|error| <= 1.5e-7); the bound checked is 3e-7 max(1, |z|)."""
+    from scipy.special import erf
+    d = 64
+    z = np.linspace(-12.0, 12.0, 64 * 1024).astype(np.float32)
+    a = torch.as_tensor(z.reshape(-1, d)).cuda()
+    rows = a.shape[0]
+    eye = torch.eye(d, device="cuda")[None].contiguous()
+    zero = torch.zeros(1, d, device="cuda")
+    hid = torch.empty(rows, d, device="cuda")
+    out = torch.empty(rows, d, device="cuda")
+    off = torch.tensor([0, rows], dtype=torch.int32, device="cuda")
+    say(f"[gpu] activation accuracy {act}")
+    api.moe_grouped_ffn(a, off, rows, eye, zero, eye, zero, act, hid, out)
+    torch.cuda.synchronize()
+    zz = z.astype(np.float64)
+    want = {"relu": np.maximum(zz, 0.0), "gelu": 0.5 * zz * (1.0 + erf(zz / np.sqrt(2.0))),
+            "swish": zz / (1.0 + np.exp(-zz))}[act]
+    got = out.cpu().numpy().reshape(-1).astype(np.float64)
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(zz))
+    assert err.max() <= (0.0 if act == "relu" else 3e-7), err.max()
+    assert torch.equal(hid, out)
+
+
 def test_shared_experts_alone():
     """Shared FFN (one FFN of width S F, segmented second layer) vs the oracle's
     expert-by-expert sum."""
