@@ -4,15 +4,16 @@
 // over ragged groups, see GemmArgs), built for throughput:
 //  * operands go global -> LDS directly (global_load_lds_dwordx4: each lane's
 //    16 bytes land at M0 + 16 * lane), no register staging;
-//  * an NS-stage LDS ring of K = 32 slabs, loads issued NS-1 slabs ahead, one
-//    barrier per slab;
-//  * slab rows are 64 bytes (K = 32) with their 16-byte chunks permuted per
-//    row (swz) so MFMA operand reads run conflict-free, while each 4 lanes of
-//    a load still fetch one row's 64 contiguous bytes;
+//  * an NS-stage LDS ring of K = 32 SUB slabs (SUB = 1 or 2), loads issued NS-1
+//    stages ahead, one barrier per stage;
+//  * stage rows are 64 SUB bytes with their 16-byte chunks permuted per row
+//    (swz) so MFMA operand reads run conflict-free, while each 4 SUB lanes of a
+//    load still fetch one row's 64 SUB contiguous bytes (SUB = 2: whole
+//    128-byte cache lines);
 //  * block tile BM x BN, WGM x WGN waves, each wave (BM/WGM) x (BN/WGN) of
 //    v_mfma_f32_16x16x32_bf16 tiles; the output is staged through LDS in
 //    16 WGM-row chunks for 16-byte stores.
-// Requires K % 32 == 0 (and, for S > 1, Kseg % 32 == 0).
+// Requires K % (32 SUB) == 0 (and, for S > 1, Kseg % (32 SUB) == 0).
 
 #include "common.h"
 #include "internal.h"
@@ -32,13 +33,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Slab rows are 64 bytes (32 bf16 of K) with their four 16-byte chunks
-// permuted: logical chunk c of row r sits at chunk c ^ swz(r).  An MFMA operand
-// read (16 lanes = 16 consecutive rows at one logical chunk) then takes the
-// minimum 4 LDS cycles per ds_read_b128; rows unpermuted, or permuted by
-// r & 3 or by (r >> 2) & 3, take 8 (measured on MI355X with LDS
-// bank-conflict counters).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// Stage rows are 64 SUB bytes (32 SUB bf16 of K) with their 16-byte chunks
+// permuted: logical chunk c of row r sits at chunk c ^ swz(r).  The LDS serves
+// a ds_read_b128 eight lanes at a time from 128 bytes of banks, so the eight
+// consecutive rows an MFMA operand read touches at one logical chunk must land
+// on eight different 16-byte bank groups.  For 64-byte rows (SUB = 1) two rows
+// share a 128-byte bank row and swz(r) = (r >> 1) & 3 separates them (4 LDS
+// cycles per ds_read_b128; unpermuted, r & 3 or (r >> 2) & 3 take 8, measured
+// on MI355X with bank-conflict counters); for 128-byte rows (SUB = 2) every
+// row spans all bank groups and swz(r) = r & 7 does.
+template <int SUB>
+__device__ __forceinline__ int swz(int r) { return SUB == 1 ? (r >> 1) & 3 : r & 7; }
 
 // Workgroup barrier for the slab ring.  It first waits for this wave's LDS
 // reads: the compiler may leave the reads of one slab in flight across the
@@ -48,29 +53,33 @@ __device__ __forceinline__ void slab_barrier() { asm volatile("s_waitcnt lgkmcnt
 
 }  // namespace
 
-template <int BM, int BN, int WGM, int WGN, int NS, bool SEG>
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, bool SEG>
 struct V2 {
   static constexpr int NW = WGM * WGN, NT = 64 * NW;     // waves, threads
   static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave tile
   static constexpr int TM = WM / 16, TN = WN / 16;       // MFMA tiles per wave
-  static constexpr int SLAB = (BM + BN) * 64;            // bytes per stage
-  static constexpr int LPW = (BM + BN) / (16 * NW);      // load instructions per wave per stage
+  static constexpr int RB = 64 * SUB;                    // bytes per stage row
+  static constexpr int KS = 32 * SUB;                    // K per stage
+  static constexpr int RPI = 1024 / RB;                  // rows per load instruction
+  static constexpr int SLAB = (BM + BN) * RB;            // bytes per stage
+  static constexpr int LPW = (BM + BN) / (RPI * NW);     // load instructions per wave per stage
   static constexpr int SR = 16 * WGM;                    // output rows staged per pass
   static constexpr int LDC = (SR * (BN + 8) * 2 <= SLAB) ? BN + 8 : BN;  // staged row (bf16)
-  static_assert((BM + BN) % (16 * NW) == 0, "slab rows must split evenly over the waves");
+  static_assert(SUB == 1 || SUB == 2, "32- or 64-wide K stages");
+  static_assert((BM + BN) % (RPI * NW) == 0, "stage rows must split evenly over the waves");
   static_assert(SR * LDC * 2 <= SLAB, "staged output rows must fit in one stage buffer");
-  static_assert(NS >= 3 && NS <= 6, "3 to 6 stages");
+  static_assert(NS >= 2 && NS <= 6, "2 to 6 stages");
 };
 
 // One LDS array per stage: distinct objects let the compiler see that reading
 // one stage does not alias the loads in flight into the others.
-template <int BM, int BN, int WGM, int WGN, int NS, int MINB, bool SEG>
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(GemmArgs p) {
-  using C = V2<BM, BN, WGM, WGN, NS, SEG>;
+  using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG>;
   constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
   __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
   __shared__ __attribute__((aligned(1024))) char st1[C::SLAB];
-  __shared__ __attribute__((aligned(1024))) char st2[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? C::SLAB : 16];
@@ -90,21 +99,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
   const int n0 = tl.nt * BN;
   const bf16_t* A = (const bf16_t*)p.A;
   const bf16_t* B = (const bf16_t*)p.B;
-  const int rep = p.a_repeat > 1 ? p.a_repeat : 1;
-  const int lda = K / rep;
 
-  // ---- this lane's load slots: instruction j = wave + NW i fills slab rows
-  // 16 j .. 16 j + 15 (1 KB); lane l fills row 16 j + l / 4, physical chunk l % 4,
-  // so each 4 lanes fetch one row's 64 contiguous bytes
+  // ---- this lane's load slots: instruction j = wave + NW i fills stage rows
+  // RPI j .. RPI j + RPI - 1 (1 KB); lane l fills row RPI j + l / (4 SUB),
+  // physical chunk l % (4 SUB), so each 4 SUB lanes fetch one row's 64 SUB
+  // contiguous bytes
   const bf16_t* src[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int row = 16 * (wave + NW * i) + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(row);  // logical chunk stored here
+    const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
+    const int chunk = (lane % (4 * SUB)) ^ swz<SUB>(row);  // logical chunk stored here
     if (row < BM) {
       const int r = row < tl.M ? row : tl.M - 1;
       const int64_t arow = p.a_rows ? (int64_t)p.a_rows[tl.row0 + r] : tl.row0 + r;
-      src[i] = A + arow * lda + chunk * 8;
+      src[i] = A + arow * K + chunk * 8;
     } else {
       const int nr = row - BM;
       const int n = (n0 + nr < N) ? n0 + nr : N - 1;
@@ -112,20 +120,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
                    : B + ((int64_t)tl.g * N + n) * K + chunk * 8;
     }
   }
-  const int nk = K / 32;
+  const int nk = K / C::KS;
   auto issue = [&](int kt, int stage) {
-    const int k = (kt < nk ? kt : nk - 1) * 32;  // past the end: harmless reload
+    const int k = (kt < nk ? kt : nk - 1) * C::KS;  // past the end: harmless reload
     char* base = stages[stage];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int row0 = 16 * (wave + NW * i);
+      const int row0 = C::RPI * (wave + NW * i);
       int64_t off = k;
-      if (row0 < BM && rep > 1) off = (k / (32 * rep)) * 32;
       if (SEG && row0 >= BM) {
         const int s = k / p.Kseg;
         off = (int64_t)s * N * p.Kseg + (k - s * p.Kseg);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + off), (lds_ptr_t)(base + row0 * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + off), (lds_ptr_t)(base + row0 * C::RB), 16, 0, 0);
     }
   };
 
@@ -135,39 +142,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // operand read offsets (bytes within a slab): lane (fr, fc) reads row fr
-  // of its 16-row tile at logical k-chunk fc
+  // operand read offsets (bytes within a stage): lane (fr, fc) reads row fr
+  // of its 16-row tile at logical k-chunk 4 h + fc of sub-slab h
   const int fr = lane & 15, fc = lane >> 4;
-  int a_rd[TM], b_rd[TN];
+  int a_rd[SUB][TM], b_rd[SUB][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int R = wm * C::WM + i * 16 + fr;
-    a_rd[i] = R * 64 + ((fc ^ swz(R)) << 4);
-  }
+  for (int h = 0; h < SUB; ++h) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int R = BM + wn * C::WN + j * 16 + fr;
-    b_rd[j] = R * 64 + ((fc ^ swz(R)) << 4);
+    for (int i = 0; i < TM; ++i) {
+      const int R = wm * C::WM + i * 16 + fr;
+      a_rd[h][i] = R * C::RB + (((4 * h + fc) ^ swz<SUB>(R)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int R = BM + wn * C::WN + j * 16 + fr;
+      b_rd[h][j] = R * C::RB + (((4 * h + fc) ^ swz<SUB>(R)) << 4);
+    }
   }
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
   auto step = [&](int kt, int stage) {
-    wait_vmcnt<(NS - 2) * LPW>();   // this wave's loads of step kt have landed
+    wait_vmcnt<(NS - 2) * LPW>();   // this wave's loads of stage kt have landed
     slab_barrier();                  // ... and every other wave's
     issue(kt + NS - 1, (stage + NS - 1) % NS);
     const char* base = stages[stage];
-    bf16x8_t a[TM], b[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[i]);
+    for (int h = 0; h < SUB; ++h) {
+      bf16x8_t a[TM], b[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[j]);
+      for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[h][i]);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[h][j]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
   };
 
   int kt = 0;
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int MINB>
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB>
 static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
   if (rows <= 0) return hipSuccess;
@@ -274,15 +287,17 @@ static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)grid_blocks(mt, (a.N + BN - 1) / BN));
   const dim3 block(64 * WGM * WGN);
   if (a.S > 1)
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, MINB, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, MINB, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 bool gemm_v2_supported(const GemmArgs& a) {
-  return a.K % 32 == 0 && (a.S <= 1 || a.Kseg % 32 == 0) && (a.a_repeat <= 1 || a.K % (32 * a.a_repeat) == 0);
+  return a.K % 32 == 0 && (a.S <= 1 || a.Kseg % 32 == 0);
 }
+
+bool gemm_v2_wide_k(const GemmArgs& a) { return a.K % 64 == 0 && (a.S <= 1 || a.Kseg % 64 == 0); }
 
 // Eight waves (2 x 4) per block and a 3-stage ring: with two or three blocks
 // resident per CU each SIMD holds four or more waves, which hides the LDS and
@@ -290,9 +305,10 @@ bool gemm_v2_supported(const GemmArgs& a) {
 // MI355X: 10-35 % faster than four waves with a 4-stage ring on the expert
 // shapes, bit-identical results).
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
-  if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 2>(a, st);
-  if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 2>(a, st);
-  return launch_v2<128, 128, 2, 4, 3, 2>(a, st);
+  if (tile == 512) return launch_v2<256, 256, 2, 4, 2, 2, 1>(a, st);
+  if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2>(a, st);
+  if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2>(a, st);
+  return launch_v2<128, 128, 2, 4, 3, 1, 2>(a, st);
 }
 
 }  // namespace moe

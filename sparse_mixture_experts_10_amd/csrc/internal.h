@@ -62,8 +62,6 @@ struct GemmArgs {
   void* C;                   // [rows, N]
   int act;                   // activation, or -1 for none
   float* sq_part;            // [max_rows][n_tiles] partial sum of squares, or nullptr
-  int a_repeat;              // > 1: each 32-wide K slab of A serves a_repeat consecutive slabs of B
-                             //      (A is [rows, K / a_repeat]); 0 or 1: plain
   bool out_f32;              // C is fp32 (no staging; bias and activation still apply)
 };
 
@@ -71,7 +69,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);     // picks the
 int gemm_bf16_n_tiles(const GemmArgs& a);                           // N tiles of that choice
 hipError_t launch_gemm_bf16_v1(const GemmArgs& a, hipStream_t st);  // any K % 8 == 0
 bool gemm_v2_supported(const GemmArgs& a);                         // K % 32 == 0
-hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st);  // tile 128 or 256
+bool gemm_v2_wide_k(const GemmArgs& a);                            // K % 64 == 0
+hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st);  // tile 64, 128, 256, 512
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_sq_reduce(const float* sq_part, int n_tiles, const int32_t* group_offset, int G,
                             int64_t max_rows, float* sq, hipStream_t st);

@@ -239,21 +239,23 @@ def test_grouped_ffn_ragged_groups(dtype, d, gather):
     np.testing.assert_allclose(f64(sq), refsq, rtol=1e-5)
 
 
-@pytest.mark.parametrize("act", ["swish", None])
-def test_grouped_gemm_repeatable_full_size(act):
-    """The expert-up pass at the fine-grained workload's full shape (64 ragged
-    groups, 49152 rows, d 2048, F 1408), run three times: the outputs agree bit
-    for bit.  Guards the LDS slab ring against reads racing the refill of
-    their stage (such a race corrupts a few scattered 16-byte chunks)."""
-    counts = torch.randint(596, 988, (64,), generator=torch.Generator().manual_seed(5))
-    off = torch.zeros(65, dtype=torch.int32)
+@pytest.mark.parametrize("act,G,lo,hi,d,F", [("swish", 64, 596, 988, 2048, 1408), (None, 64, 596, 988, 2048, 1408),
+                                              ("gelu", 16, 1800, 2300, 1024, 1536)])
+def test_grouped_gemm_repeatable_full_size(act, G, lo, hi, d, F):
+    """The expert-up pass at full expert shapes (the fine-grained workload's 64
+    ragged groups of ~768 rows, d 2048, F 1408; and 16 groups of ~2048 rows,
+    which take the 256 x 256 tiles), run three times: the outputs agree bit for
+    bit.  Guards the LDS stage ring against reads racing the refill of their
+    stage (such a race corrupts a few scattered 16-byte chunks)."""
+    counts = torch.randint(lo, hi, (G,), generator=torch.Generator().manual_seed(5))
+    off = torch.zeros(G + 1, dtype=torch.int32)
     off[1:] = torch.cumsum(counts, 0)
-    rows, d, F = int(off[-1]), 2048, 1408
-    say(f"[gpu] grouped gemm repeatability rows={rows} d={d} F={F} act={act}")
+    rows = int(off[-1])
+    say(f"[gpu] grouped gemm repeatability G={G} rows={rows} d={d} F={F} act={act}")
     g = torch.Generator(device="cuda").manual_seed(6)
     a = torch.randn(rows, d, device="cuda", generator=g).to(torch.bfloat16)
-    W1 = (torch.randn(64, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
-    b1 = (0.1 * torch.randn(64, F, device="cuda", generator=g)).to(torch.bfloat16)
+    W1 = (torch.randn(G, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(G, F, device="cuda", generator=g)).to(torch.bfloat16)
     goff = off.cuda()
     outs = []
     for _ in range(3):
@@ -268,13 +270,15 @@ def test_grouped_gemm_repeatable_full_size(act):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     # spot-check the first and last row of every group against a float64 product
     got, want = [], []
-    for gi in range(64):
+    for gi in range(G):
         Wg = W1[gi].double().cpu()
         bg = b1[gi].double().cpu()
         for r in (int(off[gi]), int(off[gi + 1]) - 1):
             z = Wg @ a[r].double().cpu() + bg
             if act == "swish":
                 z = z * torch.sigmoid(z)
+            elif act == "gelu":
+                z = 0.5 * z * (1.0 + torch.erf(z / 2.0 ** 0.5))
             want.append(z.numpy())
             got.append(f64(outs[0][r]))
     close_out(np.stack(got), np.stack(want), "bf16", "grouped gemm rows")
