@@ -18,7 +18,7 @@ Sources, cited by page title and section:
                 "Configuration", "The gating / routing path", "Load balancing",
                 "Minimal example".
   [Credit]      "Sparse MoE Expert-Credit Loss Reweighting Diagram":
-                "What the diagram shows", panel (b).
+                "What the diagram shows", panels (b) and (c).
 
 Parity status: every function here is pinned by a CPU test against a closed
 form, an invariant, a textbook routine or brute force (tests/test_oracle_*.py).
@@ -26,6 +26,8 @@ form, an invariant, a textbook routine or brute force (tests/test_oracle_*.py).
 from .moe import (ACTIVATIONS, OracleResult, activation, capacity, combine, credit,
                   dispatch, expert_ffn, forward, gates, near_tie_gap, route_stats,
                   router_logits, softmax_lse, topk)
+from .balance import (balance_losses, cv_squared, dro_update, expert_attributed_loss, importance,
+                      selection_bias_update)
 from .dense import dense_dispatch_combine, dense_softmax_mixture
 from .brute import brute_topk
 
@@ -33,5 +35,6 @@ __all__ = [
     "ACTIVATIONS", "OracleResult", "activation", "capacity", "combine", "credit",
     "dispatch", "expert_ffn", "forward", "gates", "near_tie_gap", "route_stats",
     "router_logits", "softmax_lse", "topk", "dense_dispatch_combine",
-    "dense_softmax_mixture", "brute_topk",
+    "dense_softmax_mixture", "brute_topk", "balance_losses", "cv_squared", "dro_update",
+    "expert_attributed_loss", "importance", "selection_bias_update",
 ]

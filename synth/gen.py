@@ -29,6 +29,7 @@ TENSOR_IDS = {
     "x": 0, "W_g": 1, "b_g": 2, "b_sel": 3,
     "W1": 4, "b1": 5, "W2": 6, "b2": 7,
     "sW1": 8, "sb1": 9, "sW2": 10, "sb2": 11,
+    "token_loss": 12,
 }
 
 
@@ -191,3 +192,11 @@ def draw(w: Workload, seed: int = SEED, threads: Optional[int] = None) -> Inputs
         inp.sW2 = _per_expert(seed, w, "sW2", S, (d, F), 1.0 / F, dt, threads)
         inp.sb2 = _store(_normal(_rng(seed, w.tag, "sb2"), (S, d), 0.01), dt)
     return inp
+
+
+def token_losses(w: Workload, seed: int = SEED) -> np.ndarray:
+    """Synthetic per-token losses [T] float32 for the credit reweighting (no
+    model exists to produce real ones): 1 + Exp(1), positive with mean 2, the
+    scale of a language model's per-token cross-entropy."""
+    rng = _rng(seed, w.tag, "token_loss")
+    return (1.0 + rng.standard_exponential(w.T, dtype=np.float32)).astype(np.float32)

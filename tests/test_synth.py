@@ -54,3 +54,11 @@ def test_unit_row_router_gives_unit_logit_std():
     inp = synth.draw(synth.LARGE_CREDIT.with_(T=2048, F=8, E=128))
     h = oracle.router_logits(synth.widen(inp.x, "bf16"), inp.W_g, None)
     assert h.std() == pytest.approx(1.0, rel=0.03)
+
+
+def test_token_losses():
+    a = synth.token_losses(synth.DEFAULT)
+    b = synth.token_losses(synth.DEFAULT)
+    assert a.dtype == np.float32 and a.shape == (synth.DEFAULT.T,)
+    assert (a == b).all() and (a >= 1.0).all()
+    assert abs(float(a.mean()) - 2.0) < 0.1
