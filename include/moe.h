@@ -73,6 +73,7 @@ extern "C" {
 #define MOE_OP_STATS 4
 #define MOE_OP_SHARED_FFN 5
 #define MOE_OP_ROUTE 6
+#define MOE_OP_BALANCE 7
 
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);
@@ -95,8 +96,8 @@ int moe_capacity(int64_t cf_num, int64_t cf_den, int32_t k, int64_t T, int32_t E
  * (0 when the operation needs none).  Host-only.  Arguments that an operation
  * does not use are ignored: ROUTER uses T, d, E (the size assumes bf16 x;
  * fp32 x needs none); DISPATCH uses T, E; FFN uses F, max_rows; STATS uses T, E,
- * k (the size covers credit); ROUTE uses T, d, E (as ROUTER plus DISPATCH plus
- * the statistics partials).
+ * k (the size covers credit and the expert-attributed loss); ROUTE uses T, d,
+ * E (as ROUTER plus DISPATCH plus the statistics partials); BALANCE uses T, E.
  */
 int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int32_t F,
                         int64_t max_rows, size_t* bytes);
@@ -263,19 +264,66 @@ int moe_combine(const void* expert_out, const int32_t* row, const float* topk_ga
  *   losses[2] = losses[0] + losses[1]
  *   credit[t,j]    = topk_gate[t,j] * sqrt(hidden_sqnorm[row[t,j]]), 0 when row = -1
  *   mean_credit[e] = (1/T) sum of credit over the kept choices of expert e
+ *   expert_loss[e] = (1/T) sum of credit * token_loss[t] over the same choices
+ *                    (the expert-attributed loss of panel (b), N = T)
  * Inputs: logits [T,E], lse [T], topk_idx [T,k], topk_gate [T,k], expert_count
  * [E] (device, from moe_router_topk / moe_dispatch).  Outputs f [E], P [E],
  * losses [3] fp32 device.  Credit is computed when credit and mean_credit are
  * both non-NULL; it then needs hidden_sqnorm [rows], row [T,k], expert_offset
- * [E+1] and row_token [rows] (device).  Sums run in fp64 in a fixed order.
+ * [E+1] and row_token [rows] (device).  The expert-attributed loss is computed
+ * when token_loss [T] fp32 and expert_loss [E] fp32 (device) are both non-NULL,
+ * and needs the credit.  Sums run in fp64 in a fixed order.
  *   ws  MOE_OP_STATS workspace.  T must be >= 1.
  */
 int moe_route_stats(const float* logits, const float* lse, const int32_t* topk_idx,
                     const float* topk_gate, const int32_t* expert_count, int64_t T, int32_t E,
                     int32_t k, float alpha, float beta, float* f, float* P, float* losses,
                     const float* hidden_sqnorm, const int32_t* row, const int32_t* expert_offset,
-                    const int32_t* row_token, float* credit, float* mean_credit, void* ws,
-                    size_t ws_bytes, hipStream_t stream);
+                    const int32_t* row_token, float* credit, float* mean_credit,
+                    const float* token_loss, float* expert_loss, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/*
+ * Coefficient-of-variation balance losses ("Code Walkthrough -- SER", Load
+ * balancing: balance across experts, total importance per expert, and the
+ * aux loss combining load_balance_coef * load_balance + z_loss_coef * z_loss):
+ *   importance[e] = sum over the batch of topk_gate[t,j] with topk_idx[t,j] = e
+ *   out[0] = CV(expert_count)^2, out[1] = CV(importance)^2  (CV^2 = population
+ *            variance / mean^2, 0 when the mean is 0)
+ *   out[2] = (1/T) sum_t lse[t]^2
+ *   out[3] = load_balance_coef * out[0] + z_loss_coef * out[2]
+ * Inputs topk_gate, topk_idx [T,k], expert_count [E] (pre-capacity), lse [T]
+ * device; outputs importance [E] and out [4] fp32 device.  Sums in fp64 in a
+ * fixed order.  ws: MOE_OP_BALANCE workspace.  T must be >= 1.
+ */
+int moe_balance_losses(const float* topk_gate, const int32_t* topk_idx, const int32_t* expert_count,
+                       const float* lse, int64_t T, int32_t E, int32_t k, float load_balance_coef,
+                       float z_loss_coef, float* importance, float* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * Aux-loss-free balancing ("Appendix C -- Acronyms & Symbols", Balancing:
+ * per-expert selection bias b_i and its update rate gamma): every expert whose
+ * pre-capacity load is below the mean load k T / E raises its bias by gamma,
+ * above it lowers it by gamma, equal keeps it:
+ *   b_sel[e] += gamma * sign(k T - E expert_count[e])   (sign exact in integers)
+ * expert_count [E] int32 device; b_sel [E] fp32 device, updated in place.
+ */
+int moe_selection_bias_update(const int32_t* expert_count, int32_t E, int32_t k, int64_t T, float gamma,
+                              float* b_sel, hipStream_t stream);
+
+/*
+ * One step of the EMA tracker and the layer-wise DRO weights ("Sparse MoE
+ * Expert-Credit Loss Reweighting Diagram", panel (c)), in this order:
+ *   ema[e] <- ema_decay * ema[e] + (1 - ema_decay) * expert_loss[e]
+ *   mu     <- softmax(mu + eta * ema)
+ *   dro_loss[0] = sum_e mu[e] * expert_loss[e]      (with the updated mu)
+ * expert_loss [E] fp32 device (e.g. from moe_route_stats); ema, mu [E] fp32
+ * device, updated in place; dro_loss [1] fp32 device.  fp64 arithmetic,
+ * fixed order.
+ */
+int moe_dro_update(const float* expert_loss, int32_t E, float ema_decay, float eta, float* ema,
+                   float* mu, float* dro_loss, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,10 @@ SIGNATURES = {
                               _P]),
     "moe_combine": (_INT, [_P, _P, _P, _P, _I64, _I32, _I32, _INT, _P, _P]),
     "moe_route_stats": (_INT, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _P, _P, _P, _P, _P,
-                               _P, _P, _P, _P, _P, _SZ, _P]),
+                               _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_balance_losses": (_INT, [_P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]),
+    "moe_selection_bias_update": (_INT, [_P, _I32, _I32, _I64, _F32, _P, _P]),
+    "moe_dro_update": (_INT, [_P, _I32, _F32, _F32, _P, _P, _P, _P]),
 }
 
 _lib = None

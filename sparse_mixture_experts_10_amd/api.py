@@ -16,7 +16,7 @@ from ._native import load
 
 MOE_F32, MOE_BF16 = 0, 1
 ACT = {"relu": 0, "gelu": 1, "swish": 2}
-OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN, OP_ROUTE = range(7)
+OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN, OP_ROUTE, OP_BALANCE = range(8)
 
 
 class MoEError(RuntimeError):
@@ -158,11 +158,31 @@ def moe_combine(expert_out, row, topk_gate, shared_out, y, stream=None):
 
 def moe_route_stats(logits, lse, topk_idx, topk_gate, expert_count, alpha, beta, f, P, losses,
                     hidden_sqnorm=None, row=None, expert_offset=None, row_token=None, credit=None,
-                    mean_credit=None, ws=None, stream=None):
+                    mean_credit=None, ws=None, stream=None, token_loss=None, expert_loss=None):
     T, E = logits.shape
     k = topk_idx.shape[1]
     wp, wn = _ws(ws)
     _check("moe_route_stats", load().moe_route_stats(
         _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), _p(expert_count), T, E, k, alpha, beta,
         _p(f), _p(P), _p(losses), _p(hidden_sqnorm), _p(row), _p(expert_offset), _p(row_token),
-        _p(credit), _p(mean_credit), wp, wn, _s(stream)))
+        _p(credit), _p(mean_credit), _p(token_loss), _p(expert_loss), wp, wn, _s(stream)))
+
+
+def moe_balance_losses(topk_gate, topk_idx, expert_count, lse, load_balance_coef, z_loss_coef, importance,
+                       out, ws, stream=None):
+    T, k = topk_idx.shape
+    E = expert_count.shape[0]
+    wp, wn = _ws(ws)
+    _check("moe_balance_losses", load().moe_balance_losses(
+        _p(topk_gate), _p(topk_idx), _p(expert_count), _p(lse), T, E, k, load_balance_coef, z_loss_coef,
+        _p(importance), _p(out), wp, wn, _s(stream)))
+
+
+def moe_selection_bias_update(expert_count, k, T, gamma, b_sel, stream=None):
+    _check("moe_selection_bias_update", load().moe_selection_bias_update(
+        _p(expert_count), expert_count.shape[0], k, T, gamma, _p(b_sel), _s(stream)))
+
+
+def moe_dro_update(expert_loss, ema_decay, eta, ema, mu, dro_loss, stream=None):
+    _check("moe_dro_update", load().moe_dro_update(
+        _p(expert_loss), expert_loss.shape[0], ema_decay, eta, _p(ema), _p(mu), _p(dro_loss), _s(stream)))

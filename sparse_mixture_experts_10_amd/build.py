@@ -22,7 +22,8 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(OUT_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "gemm_bf16_v2.hip", "combine.hip", "stats.hip", "abi.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "gemm_bf16_v2.hip", "combine.hip", "stats.hip", "balance.hip",
+           "abi.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

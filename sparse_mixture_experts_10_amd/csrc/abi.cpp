@@ -72,8 +72,10 @@ size_t stats_ws_parts(int64_t T, int32_t E) {
   return align_up((size_t)nparts * (size_t)(E + 1) * sizeof(double));
 }
 
+size_t stats_row_bytes(int64_t T, int32_t k) { return align_up((size_t)T * (size_t)k * sizeof(float)); }
+
 size_t stats_ws(int64_t T, int32_t E, int32_t k, bool credit) {
-  return stats_ws_parts(T, E) + (credit ? align_up((size_t)T * (size_t)k * sizeof(float)) : 0);
+  return stats_ws_parts(T, E) + (credit ? 2 * stats_row_bytes(T, k) : 0);
 }
 
 }  // namespace
@@ -132,6 +134,10 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
       if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
       if (k < 1) return MOE_ERR_INVALID_ARG;
       *bytes = stats_ws(T, E, k, true);
+      return MOE_OK;
+    case MOE_OP_BALANCE:
+      if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = stats_ws_parts(T, E);
       return MOE_OK;
     case MOE_OP_ROUTE:
       if (T < 0 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
@@ -357,8 +363,9 @@ int moe_route_stats(const float* logits, const float* lse, const int32_t* topk_i
                     const float* topk_gate, const int32_t* expert_count, int64_t T, int32_t E,
                     int32_t k, float alpha, float beta, float* f, float* P, float* losses,
                     const float* hidden_sqnorm, const int32_t* row, const int32_t* expert_offset,
-                    const int32_t* row_token, float* credit, float* mean_credit, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
+                    const int32_t* row_token, float* credit, float* mean_credit,
+                    const float* token_loss, float* expert_loss, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
   if (T < 1) return MOE_ERR_INVALID_ARG;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
@@ -366,12 +373,47 @@ int moe_route_stats(const float* logits, const float* lse, const int32_t* topk_i
     return MOE_ERR_INVALID_ARG;
   if ((credit == nullptr) != (mean_credit == nullptr)) return MOE_ERR_INVALID_ARG;
   if (credit && (!hidden_sqnorm || !row || !expert_offset || !row_token)) return MOE_ERR_INVALID_ARG;
+  if ((token_loss == nullptr) != (expert_loss == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (token_loss && !credit) return MOE_ERR_INVALID_ARG;   // the loss is weighted by the credit
   const size_t need = stats_ws(T, E, k, credit != nullptr);
   if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
-  float* credit_row = credit ? (float*)((char*)ws + stats_ws_parts(T, E)) : nullptr;
+  char* rows = (char*)ws + stats_ws_parts(T, E);
+  float* credit_row = credit ? (float*)rows : nullptr;
+  float* loss_row = token_loss ? (float*)(rows + stats_row_bytes(T, k)) : nullptr;
   return hip_status(launch_stats(logits, lse, topk_idx, topk_gate, expert_count, T, E, k, alpha,
                                  beta, f, P, losses, hidden_sqnorm, row, expert_offset, row_token,
-                                 credit, mean_credit, (double*)ws, credit_row, stream));
+                                 credit, mean_credit, (double*)ws, credit_row, token_loss, loss_row,
+                                 expert_loss, stream));
+}
+
+int moe_balance_losses(const float* topk_gate, const int32_t* topk_idx, const int32_t* expert_count,
+                       const float* lse, int64_t T, int32_t E, int32_t k, float load_balance_coef,
+                       float z_loss_coef, float* importance, float* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (int rc = check_ek(E, k)) return rc;
+  if (T < 1) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!topk_gate || !topk_idx || !expert_count || !lse || !importance || !out) return MOE_ERR_INVALID_ARG;
+  const size_t need = stats_ws_parts(T, E);
+  if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_balance(topk_gate, topk_idx, expert_count, lse, T, E, k, load_balance_coef,
+                                   z_loss_coef, importance, out, (double*)ws, stream));
+}
+
+int moe_selection_bias_update(const int32_t* expert_count, int32_t E, int32_t k, int64_t T, float gamma,
+                              float* b_sel, hipStream_t stream) {
+  if (int rc = check_ek(E, k)) return rc;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!expert_count || !b_sel) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(expert_count, E, k, T, gamma, b_sel, stream));
+}
+
+int moe_dro_update(const float* expert_loss, int32_t E, float ema_decay, float eta, float* ema,
+                   float* mu, float* dro_loss, hipStream_t stream) {
+  if (E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!expert_loss || !ema || !mu || !dro_loss) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dro_update(expert_loss, E, ema_decay, eta, ema, mu, dro_loss, stream));
 }
 
 }  // extern "C"

@@ -79,12 +79,23 @@ hipError_t launch_combine(const void* expert_out, const int32_t* row, const floa
                           const void* shared_out, int64_t T, int k, int d_out, bool bf16,
                           void* y, hipStream_t st);
 
-// workspace: partial [nblocks][E+1] double; credit_row [rows] float (credit only)
+// workspace: partial [nblocks][E+1] double; credit_row [rows] and loss_row [rows] float
+// (credit only; loss_row only with per-token losses)
 hipError_t launch_stats(const float* logits, const float* lse, const int32_t* idx,
                         const float* gate, const int32_t* count, int64_t T, int E, int k,
                         float alpha, float beta, float* f, float* Pm, float* losses,
                         const float* sq, const int32_t* row, const int32_t* offset,
                         const int32_t* row_token, float* credit, float* mean_credit,
-                        double* ws_partial, float* credit_row, hipStream_t st);
+                        double* ws_partial, float* credit_row, const float* token_loss,
+                        float* loss_row, float* expert_loss, hipStream_t st);
+
+// workspace: partial [nblocks][E+1] double
+hipError_t launch_balance(const float* gate, const int32_t* idx, const int32_t* count,
+                          const float* lse, int64_t T, int E, int k, float lb_coef, float z_coef,
+                          float* importance, float* out, double* ws_partial, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* count, int E, int k, int64_t T, float gamma,
+                              float* b_sel, hipStream_t st);
+hipError_t launch_dro_update(const float* loss, int E, float decay, float eta, float* ema, float* mu,
+                             float* dro_loss, hipStream_t st);
 
 }  // namespace moe

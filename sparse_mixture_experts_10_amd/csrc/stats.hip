@@ -10,6 +10,8 @@
 //   credit[t,j]    = g[t,j] * ||a_{t,j}||_2   (a = the expert's hidden activation;
 //                                             0 for a dropped choice)
 //   mean_credit_e  = (1/T) sum of credit over the kept choices of expert e
+//   expert_loss_e  = (1/T) sum of credit * token_loss[t] over the same choices
+//                    (the expert-attributed loss, when per-token losses are given)
 //
 // Deterministic: no floating-point atomics.  Kernel 1 gives every block of 256
 // tokens fixed-order partial sums (fp64) of softmax mass per expert and of
@@ -26,7 +28,8 @@ namespace moe {
 __global__ __launch_bounds__(256) void stats_partial_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse, int64_t T, int E, int k,
     const float* __restrict__ gate, const float* __restrict__ sq, const int32_t* __restrict__ row,
-    float* __restrict__ credit, double* __restrict__ part, float* __restrict__ credit_row) {
+    float* __restrict__ credit, double* __restrict__ part, float* __restrict__ credit_row,
+    const float* __restrict__ token_loss, float* __restrict__ loss_row) {
   __shared__ double s_red[256];
   const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
   const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
@@ -37,7 +40,10 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
       const int r = row[t * k + j];
       const float c = r >= 0 ? gate[t * k + j] * sqrtf(sq[r]) : 0.f;
       credit[t * k + j] = c;
-      if (r >= 0) credit_row[r] = c;
+      if (r >= 0) {
+        credit_row[r] = c;
+        if (token_loss != nullptr) loss_row[r] = c * token_loss[t];
+      }
     }
   }
 }
@@ -47,7 +53,8 @@ __global__ __launch_bounds__(256) void stats_final_kernel(
     const double* __restrict__ part, int nparts, const int32_t* __restrict__ count, int64_t T,
     int E, int k, float alpha, float beta, float* __restrict__ f, float* __restrict__ Pm,
     float* __restrict__ losses, const int32_t* __restrict__ offset,
-    const float* __restrict__ credit_row, float* __restrict__ mean_credit) {
+    const float* __restrict__ credit_row, float* __restrict__ mean_credit,
+    const float* __restrict__ loss_row, float* __restrict__ expert_loss) {
   __shared__ double s_red[256];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
@@ -76,6 +83,18 @@ __global__ __launch_bounds__(256) void stats_final_kernel(
     __syncthreads();
   }
   if (tid == 0) mean_credit[e] = (float)(s_red[0] / (double)T);
+  if (expert_loss == nullptr) return;  // uniform
+  // expert-attributed loss: the same order over credit * token loss
+  __syncthreads();
+  double q = 0.0;
+  for (int64_t rr = r0 + tid; rr < r1; rr += 256) q += (double)loss_row[rr];
+  s_red[tid] = q;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] += s_red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) expert_loss[e] = (float)(s_red[0] / (double)T);
 }
 
 hipError_t launch_stats(const float* logits, const float* lse, const int32_t* idx,
@@ -83,15 +102,17 @@ hipError_t launch_stats(const float* logits, const float* lse, const int32_t* id
                         float alpha, float beta, float* f, float* Pm, float* losses,
                         const float* sq, const int32_t* row, const int32_t* offset,
                         const int32_t* row_token, float* credit, float* mean_credit,
-                        double* ws_partial, float* credit_row, hipStream_t st) {
+                        double* ws_partial, float* credit_row, const float* token_loss,
+                        float* loss_row, float* expert_loss, hipStream_t st) {
   (void)idx;
   (void)row_token;
   const int64_t nparts = (T + kStatsTokens - 1) / kStatsTokens;
   hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)nparts), dim3(256), 0, st, logits, lse, T,
-                     E, k, gate, sq, row, credit, ws_partial, credit_row);
+                     E, k, gate, sq, row, credit, ws_partial, credit_row, token_loss, loss_row);
   const unsigned nblk = mean_credit != nullptr ? (unsigned)(E + 1) : 1u;
   hipLaunchKernelGGL(stats_final_kernel, dim3(nblk), dim3(256), 0, st, ws_partial, (int)nparts, count,
-                     T, E, k, alpha, beta, f, Pm, losses, offset, credit_row, mean_credit);
+                     T, E, k, alpha, beta, f, Pm, losses, offset, credit_row, mean_credit, loss_row,
+                     expert_loss);
   return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ def close_out(gpu, ref, dtype, what):
 class Report:
     flips: List[int] = field(default_factory=list)
     notes: dict = field(default_factory=dict)
+    ref: Optional[object] = None           # the oracle result the layer was compared with
 
 
 def check_layer(inp: synth.Inputs, o, tokens: Optional[Sequence[int]] = None) -> Report:
@@ -100,6 +101,7 @@ def check_layer(inp: synth.Inputs, o, tokens: Optional[Sequence[int]] = None) ->
     rep.flips = diff.tolist()
     if len(diff):
         ref = oracle.forward(inp, tokens=tokens, topk_override=gidx)
+    rep.ref = ref
 
     # routing values
     rep.notes["logits"] = close_stat(f64(o.logits), ref.logits, "logits")

@@ -197,15 +197,29 @@ def test_shared_combine_stats_validation():
     assert lib.moe_combine(FAKE, FAKE, FAKE, MIS, 4, 2, 8, 1, FAKE, None) == INVALID
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 0, 2, 8, 1, FAKE, None) == OK
 
-    def stats(T=16, E=4, k=2, credit=NULL, mc=NULL, sq=NULL, ws=FAKE, wsb=1 << 20):
+    def stats(T=16, E=4, k=2, credit=NULL, mc=NULL, sq=NULL, tl=NULL, el=NULL, ws=FAKE, wsb=1 << 20):
         return lib.moe_route_stats(FAKE, FAKE, FAKE, FAKE, FAKE, T, E, k, 0.01, 1e-3, FAKE, FAKE, FAKE, sq,
-                                   FAKE, FAKE, FAKE, credit, mc, ws, wsb, None)
+                                   FAKE, FAKE, FAKE, credit, mc, tl, el, ws, wsb, None)
     assert stats(T=0) == INVALID
     assert stats(k=5) == INVALID
     assert stats(credit=FAKE) == INVALID       # credit and mean_credit go together
     assert stats(credit=FAKE, mc=FAKE) == INVALID   # credit needs the hidden sums of squares
     assert stats(ws=NULL) == WORKSPACE
     assert stats(wsb=8) == WORKSPACE
+    assert stats(tl=FAKE) == INVALID                # token_loss and expert_loss go together
+    assert stats(tl=FAKE, el=FAKE) == INVALID       # the expert loss needs the credit
+    assert lib.moe_balance_losses(FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 0.01, 1e-3, FAKE, FAKE, FAKE, 1 << 20,
+                                  None) == INVALID
+    assert lib.moe_balance_losses(FAKE, FAKE, FAKE, FAKE, 16, 4, 2, 0.01, 1e-3, FAKE, FAKE, NULL, 0,
+                                  None) == WORKSPACE
+    assert lib.moe_balance_losses(FAKE, FAKE, FAKE, NULL, 16, 4, 2, 0.01, 1e-3, FAKE, FAKE, FAKE, 1 << 20,
+                                  None) == INVALID
+    assert lib.moe_selection_bias_update(FAKE, 4, 5, 16, 0.1, FAKE, None) == INVALID
+    assert lib.moe_selection_bias_update(FAKE, 4, 2, 16, 0.1, NULL, None) == INVALID
+    assert lib.moe_dro_update(FAKE, 0, 0.9, 0.1, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_dro_update(FAKE, 300, 0.9, 0.1, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.moe_dro_update(FAKE, 8, 0.9, 0.1, FAKE, NULL, FAKE, None) == INVALID
+    assert api.moe_workspace_bytes(api.OP_BALANCE, T=1000, E=16) >= 4 * 17 * 8
 
 
 def test_binding_refuses_cpu_tensors():
