@@ -24,8 +24,8 @@ Parity status: every function here is pinned by a CPU test against a closed
 form, an invariant, a textbook routine or brute force (tests/test_oracle_*.py).
 """
 from .moe import (ACTIVATIONS, OracleResult, activation, capacity, combine, credit,
-                  dispatch, expert_ffn, forward, gates, near_tie_gap, route_stats,
-                  router_logits, softmax_lse, topk)
+                  dispatch, expert_ffn, forward, gates, mlp_gate_logits, near_tie_gap, noisy_logits,
+                  route_stats, router_logits, softmax_lse, topk)
 from .balance import (balance_losses, cv_squared, dro_update, expert_attributed_loss, importance,
                       selection_bias_update)
 from .dense import dense_dispatch_combine, dense_softmax_mixture
@@ -34,7 +34,7 @@ from .brute import brute_topk
 __all__ = [
     "ACTIVATIONS", "OracleResult", "activation", "capacity", "combine", "credit",
     "dispatch", "expert_ffn", "forward", "gates", "near_tie_gap", "route_stats",
-    "router_logits", "softmax_lse", "topk", "dense_dispatch_combine",
+    "router_logits", "softmax_lse", "topk", "mlp_gate_logits", "noisy_logits", "dense_dispatch_combine",
     "dense_softmax_mixture", "brute_topk", "balance_losses", "cv_squared", "dro_update",
     "expert_attributed_loss", "importance", "selection_bias_update",
 ]

@@ -4,6 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 The pass, step by step, with the passage each step follows:
   1. router logits h = W_g x (+ router bias)       [Appendix C, Core MoE symbols; SER, gating path]
+     or the optional MLP gate, plus the optional training noise of noisy top-k
+                                                    [SER, Configuration; gating path]
   2. P = softmax(h), lse = log sum_i e^{h_i}       [Appendix C, Core MoE symbols; Balancing (z-loss)]
   3. T_k(x) = the k experts with the highest scores, score = h + b_sel
                                                     [Appendix C, Core MoE symbols and Balancing (b_i);
@@ -75,6 +77,29 @@ def router_logits(x: np.ndarray, W_g: np.ndarray, b_g: Optional[np.ndarray]) -> 
     if b_g is not None:
         h = h + np.asarray(b_g, np.float64)[None, :]
     return h
+
+
+def mlp_gate_logits(x: np.ndarray, gW1: np.ndarray, gb1: np.ndarray, gW2: np.ndarray,
+                    gb2: np.ndarray) -> np.ndarray:
+    """h = gW2 relu(gW1 x + gb1) + gb2 for every token row of x.
+
+    [SER, Configuration: use_mlp_gater, gater_hidden_dim; gating path: logits
+    come from the linear router or the optional MLP gate]  Readings: a
+    two-layer MLP with biases, hidden width gater_hidden_dim, ReLU between.
+    """
+    a = np.asarray(x, np.float64) @ np.asarray(gW1, np.float64).T + np.asarray(gb1, np.float64)[None, :]
+    return np.maximum(a, 0.0) @ np.asarray(gW2, np.float64).T + np.asarray(gb2, np.float64)[None, :]
+
+
+def noisy_logits(h: np.ndarray, noise: np.ndarray, sigma: float) -> np.ndarray:
+    """h + sigma * eps with eps the supplied standard-normal draws [T, E].
+
+    [SER, gating path: noisy top-k adds training noise to the logits before
+    selection]  Readings: Gaussian noise of a fixed std sigma; the noisy
+    logits replace the logits for everything after them (softmax, lse,
+    selection, gates, statistics).
+    """
+    return np.asarray(h, np.float64) + float(sigma) * np.asarray(noise, np.float64)
 
 
 def softmax_lse(h: np.ndarray):
@@ -313,7 +338,12 @@ def forward(inp: Inputs, tokens: Optional[Sequence[int]] = None,
     dt = w.dtype
     T, E, k = w.T, w.E, w.k
     x = widen(inp.x, dt)
-    h = router_logits(x, inp.W_g, inp.b_g)
+    if w.mlp_gate:
+        h = mlp_gate_logits(x, inp.gW1, inp.gb1, inp.gW2, inp.gb2)
+    else:
+        h = router_logits(x, inp.W_g, inp.b_g)
+    if w.router_noise is not None:
+        h = noisy_logits(h, inp.noise, w.router_noise)
     P, lse = softmax_lse(h)
     idx = topk(h, k, inp.b_sel) if topk_override is None else np.asarray(topk_override, np.int64)
     gap = near_tie_gap(h, k, inp.b_sel)

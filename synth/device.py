@@ -23,7 +23,7 @@ def to_torch(inp: Inputs, device="cuda") -> Dict[str, Optional[torch.Tensor]]:
     dt = inp.dtype
     out = {name: tensor(getattr(inp, name), dt, device)
            for name in ("x", "W1", "b1", "W2", "b2", "sW1", "sb1", "sW2", "sb2")}
-    for name in ("W_g", "b_g", "b_sel"):
+    for name in ("W_g", "b_g", "b_sel", "noise", "gW1", "gb1", "gW2", "gb2"):
         a = getattr(inp, name)
         out[name] = None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
     return out

@@ -30,6 +30,7 @@ TENSOR_IDS = {
     "W1": 4, "b1": 5, "W2": 6, "b2": 7,
     "sW1": 8, "sb1": 9, "sW2": 10, "sb2": 11,
     "token_loss": 12,
+    "noise": 13, "gW1": 14, "gb1": 15, "gW2": 16, "gb2": 17,
 }
 
 
@@ -119,6 +120,11 @@ class Inputs:
     sb1: Optional[np.ndarray] = None  # [S, F]
     sW2: Optional[np.ndarray] = None  # [S, d, F]
     sb2: Optional[np.ndarray] = None  # [S, d]
+    noise: Optional[np.ndarray] = None  # [T, E] fp32 standard-normal draws (noisy top-k)
+    gW1: Optional[np.ndarray] = None    # [H, d] fp32 MLP gate
+    gb1: Optional[np.ndarray] = None    # [H]
+    gW2: Optional[np.ndarray] = None    # [E, H]
+    gb2: Optional[np.ndarray] = None    # [E]
     extra: Dict[str, object] = field(default_factory=dict)
 
     @property
@@ -191,6 +197,14 @@ def draw(w: Workload, seed: int = SEED, threads: Optional[int] = None) -> Inputs
         inp.sb1 = _store(_normal(_rng(seed, w.tag, "sb1"), (S, F), 0.01), dt)
         inp.sW2 = _per_expert(seed, w, "sW2", S, (d, F), 1.0 / F, dt, threads)
         inp.sb2 = _store(_normal(_rng(seed, w.tag, "sb2"), (S, d), 0.01), dt)
+    if w.router_noise is not None:
+        inp.noise = _normal(_rng(seed, w.tag, "noise"), (T, E), 1.0)
+    H = w.mlp_gate
+    if H:
+        inp.gW1 = _normal(_rng(seed, w.tag, "gW1"), (H, d), 1.0 / d)
+        inp.gb1 = _normal(_rng(seed, w.tag, "gb1"), (H,), 0.01)
+        inp.gW2 = _normal(_rng(seed, w.tag, "gW2"), (E, H), 1.0 / H)
+        inp.gb2 = _normal(_rng(seed, w.tag, "gb2"), (E,), 0.01)
     return inp
 
 

@@ -51,6 +51,12 @@ class Workload:
     router_bias: Optional[str] = None
     # selection-only bias: None or "uniform:<a>" = U(-a, a)
     sel_bias: Optional[str] = None
+    # noisy top-k: None (greedy) or the std sigma of the Gaussian noise added
+    # to the router logits (the standard-normal draws are an input)
+    router_noise: Optional[float] = None
+    # router form: 0 = linear router W_g x + b_g; H > 0 = MLP gate of hidden
+    # width H (its weights are inputs gW1 [H, d], gb1 [H], gW2 [E, H], gb2 [E])
+    mlp_gate: int = 0
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
