@@ -74,6 +74,7 @@ extern "C" {
 #define MOE_OP_SHARED_FFN 5
 #define MOE_OP_ROUTE 6
 #define MOE_OP_BALANCE 7
+#define MOE_OP_MLP_ROUTER 8
 
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);
@@ -97,7 +98,8 @@ int moe_capacity(int64_t cf_num, int64_t cf_den, int32_t k, int64_t T, int32_t E
  * does not use are ignored: ROUTER uses T, d, E (the size assumes bf16 x;
  * fp32 x needs none); DISPATCH uses T, E; FFN uses F, max_rows; STATS uses T, E,
  * k (the size covers credit and the expert-attributed loss); ROUTE uses T, d,
- * E (as ROUTER plus DISPATCH plus the statistics partials); BALANCE uses T, E.
+ * E (as ROUTER plus DISPATCH plus the statistics partials); BALANCE uses T, E;
+ * MLP_ROUTER uses T and F = the gate's hidden width H.
  */
 int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int32_t F,
                         int64_t max_rows, size_t* bytes);
@@ -111,6 +113,11 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
  *   x        [T, d] device, x_dtype MOE_F32 or MOE_BF16
  *   W_g      [E, d] fp32 device;  b_g [E] fp32 device or NULL (router bias, part of h)
  *   b_sel    [E] fp32 device or NULL: added to h for the selection only
+ *   noise    [T, E] fp32 device or NULL: noisy top-k ("Code Walkthrough -- SER",
+ *            The gating / routing path: training noise is added to the logits
+ *            before selection).  The logits become h + noise_std * noise and
+ *            everything below uses them.  noise holds standard-normal draws
+ *            supplied by the caller; NULL = greedy.
  *   logits   [T, E] fp32 out: h (without b_sel)
  *   lse      [T] fp32 out: log sum_e exp(h_e)
  *   topk_idx [T, k] int32 out: selected experts ordered by (h + b_sel desc,
@@ -126,8 +133,9 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
  * float64 rounding.  Logits are rounded to fp32 once.  T = 0 is a no-op.
  */
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
-                    const float* b_g, const float* b_sel, int32_t E, int32_t k, float* logits,
-                    float* lse, int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
+                    const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
+                    float noise_std, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
+                    void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
 /*
@@ -157,21 +165,41 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
                  void* x_disp, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Router with the optional MLP gate ("Code Walkthrough -- SER", Configuration:
+ * use_mlp_gater with gater_hidden_dim; The gating / routing path: the logits
+ * come from the linear router or the MLP gate):
+ *   h = gW2 relu(gW1 x + gb1) + gb2   (hidden width H, evaluated in fp64)
+ * then softmax, lse, top-k and gates exactly as moe_router_topk (b_sel and
+ * noise likewise).
+ *   gW1 [H, d], gb1 [H] or NULL, gW2 [E, H], gb2 [E] or NULL: fp32 device
+ *   H % 8 == 0, H <= 256
+ *   ws  MOE_OP_MLP_ROUTER workspace (the fp64 hidden layer, T x H).
+ * T = 0 is a no-op.
+ */
+int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* gW1,
+                        const float* gb1, int32_t H, const float* gW2, const float* gb2,
+                        const float* b_sel, int32_t E, int32_t k, const float* noise, float noise_std,
+                        float* logits, float* lse, int32_t* topk_idx, float* topk_gate, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
  * The whole routing half of the layer in one call: moe_router_topk, then an
  * index-only moe_dispatch, then the statistics f, P and losses of
  * moe_route_stats (without credit), in three kernels.  Outputs are bit-identical
  * to those three calls.  ("Appendix C -- Acronyms & Symbols", Core MoE symbols,
  * Balancing, Capacity & communication; "Code Walkthrough -- SER", The gating /
  * routing path and Load balancing.)
- *   x, W_g, b_g, b_sel, logits, lse, topk_idx, topk_gate: as moe_router_topk
+ *   x, W_g, b_g, b_sel, noise, noise_std, logits, lse, topk_idx, topk_gate:
+ *        as moe_router_topk
  *   capacity, expert_count, expert_offset, slot, row, row_token: as moe_dispatch
  *   alpha, beta, f, P, losses: as moe_route_stats
  *   ws   MOE_OP_ROUTE workspace (256-byte aligned).
  * T = 0 writes zero counts and offsets and nothing else.
  */
 int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
-              const float* b_g, const float* b_sel, int32_t E, int32_t k, int64_t capacity,
-              float alpha, float beta, float* logits, float* lse, int32_t* topk_idx,
+              const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
+              float noise_std, int64_t capacity, float alpha, float beta, float* logits, float* lse,
+              int32_t* topk_idx,
               float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
               int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
               size_t ws_bytes, hipStream_t stream);

@@ -22,12 +22,14 @@ SIGNATURES = {
     "moe_version": (_INT, []),
     "moe_capacity": (_INT, [_I64, _I64, _I32, _I64, _I32, ctypes.POINTER(_I64)]),
     "moe_workspace_bytes": (_INT, [_INT, _I64, _I32, _I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)]),
-    "moe_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
-                               _P]),
+    "moe_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _P, _P, _P, _P,
+                               _P, _SZ, _P]),
+    "moe_mlp_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _F32,
+                                   _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (_INT, [_P, _I64, _I32, _I32, _I64, _P, _INT, _I32, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
-    "moe_route": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _I64, _F32, _F32] + [_P] * 12
-                  + [_P, _SZ, _P]),
+    "moe_route": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _I64, _F32, _F32]
+                  + [_P] * 12 + [_P, _SZ, _P]),
     "moe_grouped_ffn": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P,
                                _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_up": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P, _SZ,

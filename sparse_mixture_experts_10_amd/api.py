@@ -16,7 +16,8 @@ from ._native import load
 
 MOE_F32, MOE_BF16 = 0, 1
 ACT = {"relu": 0, "gelu": 1, "swish": 2}
-OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN, OP_ROUTE, OP_BALANCE = range(8)
+(OP_ROUTER, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_STATS, OP_SHARED_FFN, OP_ROUTE, OP_BALANCE,
+ OP_MLP_ROUTER) = range(9)
 
 
 class MoEError(RuntimeError):
@@ -80,13 +81,25 @@ def moe_workspace_bytes(op: int, T: int = 0, d: int = 0, E: int = 1, k: int = 1,
     return out.value
 
 
-def moe_router_topk(x, W_g, b_g, b_sel, k, logits, lse, topk_idx, topk_gate, ws=None, stream=None):
+def moe_router_topk(x, W_g, b_g, b_sel, k, logits, lse, topk_idx, topk_gate, ws=None, stream=None,
+                    noise=None, noise_std=0.0):
     T, d = x.shape
     E = W_g.shape[0]
     wp, wn = _ws(ws)
     _check("moe_router_topk", load().moe_router_topk(
-        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(logits), _p(lse), _p(topk_idx),
-        _p(topk_gate), wp, wn, _s(stream)))
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, _p(logits), _p(lse),
+        _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
+
+
+def moe_mlp_router_topk(x, gW1, gb1, gW2, gb2, b_sel, k, logits, lse, topk_idx, topk_gate, ws, stream=None,
+                        noise=None, noise_std=0.0):
+    T, d = x.shape
+    H = gW1.shape[0]
+    E = gW2.shape[0]
+    wp, wn = _ws(ws)
+    _check("moe_mlp_router_topk", load().moe_mlp_router_topk(
+        _p(x), _dt(x), T, d, _p(gW1), _p(gb1), H, _p(gW2), _p(gb2), _p(b_sel), E, k, _p(noise), noise_std,
+        _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
 
 
 def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, row, row_token,
@@ -101,12 +114,14 @@ def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, ro
 
 
 def moe_route(x, W_g, b_g, b_sel, k, capacity, alpha, beta, logits, lse, topk_idx, topk_gate,
-              expert_count, expert_offset, slot, row, row_token, f, P, losses, ws, stream=None):
+              expert_count, expert_offset, slot, row, row_token, f, P, losses, ws, stream=None, noise=None,
+              noise_std=0.0):
     T, d = x.shape
     E = W_g.shape[0]
     wp, wn = _ws(ws)
     _check("moe_route", load().moe_route(
-        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, capacity, alpha, beta, _p(logits),
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, capacity, alpha, beta,
+        _p(logits),
         _p(lse), _p(topk_idx), _p(topk_gate), _p(expert_count), _p(expert_offset), _p(slot), _p(row),
         _p(row_token), _p(f), _p(P), _p(losses), wp, wn, _s(stream)))
 

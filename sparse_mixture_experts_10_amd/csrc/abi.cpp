@@ -135,6 +135,10 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
       if (k < 1) return MOE_ERR_INVALID_ARG;
       *bytes = stats_ws(T, E, k, true);
       return MOE_OK;
+    case MOE_OP_MLP_ROUTER:
+      if (T < 0 || F < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = mlp_router_ws_bytes(T, F);
+      return MOE_OK;
     case MOE_OP_BALANCE:
       if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
       *bytes = stats_ws_parts(T, E);
@@ -149,9 +153,9 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
 }
 
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
-                    const float* b_g, const float* b_sel, int32_t E, int32_t k, float* logits,
-                    float* lse, int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
+                    float noise_std, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
   if (T < 0 || d < 1 || d % 8 != 0) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
@@ -164,7 +168,27 @@ int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const floa
     if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
   }
   return hip_status(launch_router(x, x_dtype == MOE_BF16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
-                                  topk_idx, topk_gate, ws, stream));
+                                  topk_idx, topk_gate, noise, (double)noise_std, ws, stream));
+}
+
+int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* gW1,
+                        const float* gb1, int32_t H, const float* gW2, const float* gb2,
+                        const float* b_sel, int32_t E, int32_t k, const float* noise, float noise_std,
+                        float* logits, float* lse, int32_t* topk_idx, float* topk_gate, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (int rc = check_ek(E, k)) return rc;
+  if (T < 0 || d < 1 || d % 8 != 0 || H < 1 || H % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (H > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !gW1 || !gW2 || !logits || !lse || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(gW1) || !aligned16(gW2)) return MOE_ERR_INVALID_ARG;
+  const size_t need = mlp_router_ws_bytes(T, H);
+  if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_mlp_router(x, x_dtype == MOE_BF16, T, d, gW1, gb1, H, gW2, gb2, b_sel, E, k,
+                                      logits, lse, topk_idx, topk_gate, noise, (double)noise_std, ws,
+                                      stream));
 }
 
 int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
@@ -190,8 +214,9 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
 }
 
 int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
-              const float* b_g, const float* b_sel, int32_t E, int32_t k, int64_t capacity,
-              float alpha, float beta, float* logits, float* lse, int32_t* topk_idx,
+              const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
+              float noise_std, int64_t capacity, float alpha, float beta, float* logits, float* lse,
+              int32_t* topk_idx,
               float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
               int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
               size_t ws_bytes, hipStream_t stream) {
@@ -213,7 +238,7 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
   const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
   if (T > 0) {
     const hipError_t e = launch_router(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse, topk_idx,
-                                       topk_gate, ws, stream);
+                                       topk_gate, noise, (double)noise_std, ws, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   RouteStats rs{logits, lse, alpha, beta, f, P, losses};

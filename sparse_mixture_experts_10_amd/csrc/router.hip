@@ -23,6 +23,8 @@
 //    in LDS, then a recursive-halving reduce-scatter leaves lane eg with the
 //    sums of its experts.  Many more tokens in flight for small E.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -75,6 +77,9 @@ __device__ __forceinline__ void group_argmax(double& s, int& e, double& h) {
 
 // Per-token epilogue.  The NXE lanes of a token hold its fp64 dot products
 // (router bias not yet added): lane eg holds experts e = eg + NXE j, j < TE.
+// With noise != nullptr the logits are h + sigma * noise[t, e] (noisy top-k,
+// page "Code Walkthrough -- SER", the gating / routing path: training noise is
+// added to the logits before selection) and everything after uses them.
 // Writes logits, lse, top-k indices and gates for token t (when live).
 // With flag_rel > 0 it returns true (on every lane of the token) when two
 // consecutive scores among the k + 1 highest (k when k = E) are closer than
@@ -87,6 +92,7 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
                                                float* __restrict__ logits, float* __restrict__ lse_out,
                                                int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_gate,
+                                               const float* __restrict__ noise, double sigma,
                                                double flag_rel = 0.0) {
   const double NEG = -__builtin_huge_val();
   double h[TE], s[TE];
@@ -95,7 +101,9 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
   for (int j = 0; j < TE; ++j) {
     const int e = eg + NXE * j;
     const bool ok = e < E;
-    h[j] = ok ? acc[j] + (bg != nullptr ? (double)bg[e] : 0.0) : NEG;
+    double hv = acc[j] + (bg != nullptr ? (double)bg[e] : 0.0);
+    if (noise != nullptr && live && ok) hv += sigma * (double)noise[t * E + e];
+    h[j] = ok ? hv : NEG;
     s[j] = ok ? h[j] + (bsel != nullptr ? (double)bsel[e] : 0.0) : NEG;
     m = fmax(m, h[j]);
   }
@@ -148,32 +156,33 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
   return near;
 }
 
-template <int EP, bool XBF16>
-__global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
-    const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
-    const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
-    float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate) {
+// x element types of the E-split layout: fp32, bf16, or fp64 (the MLP gate's
+// hidden layer)
+enum { XT_F32 = 0, XT_BF16 = 1, XT_F64 = 2 };
+
+template <int XT>
+using XStage = typename std::conditional<XT == XT_F64, double, float>::type;
+
+// The E-split dot products of one block: 64 tokens x EP rows of W, fp64
+// accumulation; x and W stream through LDS in KC-wide chunks of d.
+template <int EP, int XT>
+__device__ __forceinline__ void router_block_dots(
+    const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg, int E, int64_t t0,
+    XStage<XT>* xs, float* ws, double (&acc)[RouterCfg<EP>::TM][RouterCfg<EP>::TE]) {
   using C = RouterCfg<EP>;
   constexpr int NT = C::NT, TE = C::TE, NXE = C::NXE, TM = C::TM, BT = C::BT, KC = C::KC;
   constexpr int LDX = KC + 1;
-  __shared__ float xs[BT * LDX];
-  __shared__ float ws[EP * LDX];
-
   const int tid = threadIdx.x;
   const int eg = tid % NXE;
   const int tg = tid / NXE;
-  const int64_t t0 = (int64_t)blockIdx.x * BT;
-
-  double acc[TM][TE];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0;
 
   for (int k0 = 0; k0 < d; k0 += KC) {
-    // stage x[t0 : t0+BT, k0 : k0+KC] as fp32
-    if (XBF16) {
+    // stage x[t0 : t0+BT, k0 : k0+KC]
+    if constexpr (XT == XT_BF16) {
       const bf16_t* x = (const bf16_t*)xv;
       constexpr int VPR = KC / 8;
       for (int v = tid; v < BT * VPR; v += NT) {
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
 #pragma unroll
         for (int q = 0; q < 8; ++q) xs[r * LDX + cv * 8 + q] = f[q];
       }
-    } else {
+    } else if constexpr (XT == XT_F32) {
       const float* x = (const float*)xv;
       constexpr int VPR = KC / 4;
       for (int v = tid; v < BT * VPR; v += NT) {
@@ -205,8 +214,20 @@ __global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
         xs[r * LDX + cv * 4 + 2] = q.z;
         xs[r * LDX + cv * 4 + 3] = q.w;
       }
+    } else {
+      const double* x = (const double*)xv;
+      constexpr int VPR = KC / 2;
+      for (int v = tid; v < BT * VPR; v += NT) {
+        const int r = v / VPR, cv = v % VPR;
+        const int64_t t = t0 + r;
+        const int col = k0 + cv * 2;
+        double2 q = make_double2(0.0, 0.0);
+        if (t < T && col < d) q = *(const double2*)(x + t * (int64_t)d + col);
+        xs[r * LDX + cv * 2 + 0] = q.x;
+        xs[r * LDX + cv * 2 + 1] = q.y;
+      }
     }
-    // stage W_g[0:EP, k0 : k0+KC]
+    // stage W[0:EP, k0 : k0+KC]
     {
       constexpr int VPR = KC / 4;
       for (int v = tid; v < EP * VPR; v += NT) {
@@ -235,13 +256,60 @@ __global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
     }
     __syncthreads();
   }
+}
 
-  // ---- per-token epilogue ----
+template <int EP, int XT>
+__global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
+    const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
+    const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
+    float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
+  using C = RouterCfg<EP>;
+  constexpr int TE = C::TE, NXE = C::NXE, TM = C::TM, BT = C::BT, LDX = C::KC + 1;
+  __shared__ XStage<XT> xs[BT * LDX];
+  __shared__ float ws[EP * LDX];
+  const int tid = threadIdx.x;
+  const int eg = tid % NXE;
+  const int tg = tid / NXE;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  double acc[TM][TE];
+  router_block_dots<EP, XT>(xv, T, d, Wg, E, t0, xs, ws, acc);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t t = t0 + tg * TM + i;
     token_epilogue<TE, NXE>(acc[i], eg, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx,
-                            topk_gate);
+                            topk_gate, noise, sigma);
+  }
+}
+
+// MLP gate, layer 1 (page "Code Walkthrough -- SER", Configuration: an MLP
+// gate of width gater_hidden_dim instead of the linear router):
+//   hidden[t, h] = relu(sum_j x[t, j] gW1[h, j] + gb1[h]) in fp64
+template <int HP, int XT>
+__global__ __launch_bounds__(RouterCfg<HP>::NT) void mlp_gate_hidden_kernel(
+    const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ gW1,
+    const float* __restrict__ gb1, int H, double* __restrict__ hidden) {
+  using C = RouterCfg<HP>;
+  constexpr int TE = C::TE, NXE = C::NXE, TM = C::TM, BT = C::BT, LDX = C::KC + 1;
+  __shared__ XStage<XT> xs[BT * LDX];
+  __shared__ float ws[HP * LDX];
+  const int tid = threadIdx.x;
+  const int eg = tid % NXE;
+  const int tg = tid / NXE;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  double acc[TM][TE];
+  router_block_dots<HP, XT>(xv, T, d, gW1, H, t0, xs, ws, acc);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t t = t0 + tg * TM + i;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int h = eg + NXE * j;
+      if (t < T && h < H) {
+        const double a = acc[i][j] + (gb1 != nullptr ? (double)gb1[h] : 0.0);
+        hidden[t * H + h] = a > 0.0 ? a : 0.0;
+      }
+    }
   }
 }
 
@@ -268,7 +336,7 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate) {
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
   extern __shared__ float wsm[];  // W_g [E][d], fp32
   const int tid = threadIdx.x;
   const int lane = tid & (KS_LPT - 1);
@@ -344,22 +412,23 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     rs_halve<EP / 8, 1>(b2, r, lane);
   }
   // for EP = 8, lanes 8..15 duplicate lanes 0..7; their expert ids lane >= 8 >= E are void
-  token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate);
+  token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
+                             noise, sigma);
 }
 
 template <int EP>
 static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                        const float* bg, const float* bsel, int E, int k,
                                        float* logits, float* lse, int32_t* idx, float* gate,
-                                       hipStream_t st) {
+                                       const float* noise, double sigma, hipStream_t st) {
   const dim3 grid((unsigned)((T + KS_TPB - 1) / KS_TPB));
   const size_t lds = (size_t)E * d * sizeof(float);
   if (xbf16)
     hipLaunchKernelGGL((router_ksplit_kernel<EP, true>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate);
+                       bsel, E, k, logits, lse, idx, gate, noise, sigma);
   else
     hipLaunchKernelGGL((router_ksplit_kernel<EP, false>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate);
+                       bsel, E, k, logits, lse, idx, gate, noise, sigma);
   return hipGetLastError();
 }
 
@@ -403,7 +472,7 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
     const float* __restrict__ part, int64_t T, int E, int k, const float* __restrict__ bg,
     const float* __restrict__ bsel, float* __restrict__ logits, float* __restrict__ lse_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ count,
-    int32_t* __restrict__ list) {
+    int32_t* __restrict__ list, const float* __restrict__ noise, double sigma) {
   constexpr int NXE = (EP >= 256) ? 32 : 16;
   constexpr int TE = EP / NXE;
   const int tid = threadIdx.x;
@@ -421,7 +490,7 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
     acc[j] = a;
   }
   const bool near = token_epilogue<TE, NXE>(acc, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
-                                            topk_idx, topk_gate, kRefineRel);
+                                            topk_idx, topk_gate, noise, sigma, kRefineRel);
   if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
 }
 
@@ -436,7 +505,8 @@ __global__ __launch_bounds__(kRefineThreads) void router_refine_kernel(
     const bf16_t* __restrict__ x, int d, const float* __restrict__ Wg, const float* __restrict__ bg,
     const float* __restrict__ bsel, int E, int k, const int32_t* __restrict__ count,
     const int32_t* __restrict__ list, float* __restrict__ logits, float* __restrict__ lse_out,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, const float* __restrict__ noise,
+    double sigma) {
   constexpr int TE = (EP + 63) / 64;
   constexpr int NWAVE = kRefineThreads / 64;
   __shared__ double s_h[EP];
@@ -479,7 +549,8 @@ __global__ __launch_bounds__(kRefineThreads) void router_refine_kernel(
         const int e = lane + 64 * j;
         acc[j] = e < E ? s_h[e] : 0.0;
       }
-      token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate);
+      token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
+                             noise, sigma);
     }
     __syncthreads();
   }
@@ -500,7 +571,7 @@ template <int EP>
 static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const float* Wg,
                                      const float* bg, const float* bsel, int E, int k,
                                      float* logits, float* lse, int32_t* idx, float* gate,
-                                     void* ws, hipStream_t st) {
+                                     const float* noise, double sigma, void* ws, hipStream_t st) {
   char* w8 = (char*)ws;
   bf16_t* Ws = (bf16_t*)w8;
   w8 += align256((size_t)3 * E * d * sizeof(bf16_t));
@@ -521,49 +592,105 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   constexpr int NXE = (EP >= 256) ? 32 : 16;
   const int64_t tpb = 256 / NXE;
   hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
-                     part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list);
+                     part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma);
   const unsigned nref = (unsigned)(T < 1024 ? T : 1024);
   hipLaunchKernelGGL((router_refine_kernel<EP>), dim3(nref), dim3(kRefineThreads), (size_t)d * sizeof(float),
-                     st, (const bf16_t*)x, d, Wg, bg, bsel, E, k, count, list, logits, lse, idx, gate);
+                     st, (const bf16_t*)x, d, Wg, bg, bsel, E, k, count, list, logits, lse, idx, gate,
+                     noise, sigma);
   return hipGetLastError();
 }
 
 template <int EP>
-static hipError_t launch_router_ep(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
+static hipError_t launch_router_ep(const void* x, int xt, int64_t T, int d, const float* Wg,
                                    const float* bg, const float* bsel, int E, int k, float* logits,
-                                   float* lse, int32_t* idx, float* gate, hipStream_t st) {
+                                   float* lse, int32_t* idx, float* gate, const float* noise,
+                                   double sigma, hipStream_t st) {
   using C = RouterCfg<EP>;
   const dim3 grid((unsigned)((T + C::BT - 1) / C::BT));
-  if (xbf16)
-    hipLaunchKernelGGL((router_kernel<EP, true>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel, E,
-                       k, logits, lse, idx, gate);
+  if (xt == XT_BF16)
+    hipLaunchKernelGGL((router_kernel<EP, XT_BF16>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel, E,
+                       k, logits, lse, idx, gate, noise, sigma);
+  else if (xt == XT_F32)
+    hipLaunchKernelGGL((router_kernel<EP, XT_F32>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel,
+                       E, k, logits, lse, idx, gate, noise, sigma);
   else
-    hipLaunchKernelGGL((router_kernel<EP, false>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel,
-                       E, k, logits, lse, idx, gate);
+    hipLaunchKernelGGL((router_kernel<EP, XT_F64>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel,
+                       E, k, logits, lse, idx, gate, noise, sigma);
   return hipGetLastError();
+}
+
+static hipError_t launch_router_e_split(const void* x, int xt, int64_t T, int d, const float* Wg,
+                                        const float* bg, const float* bsel, int E, int k,
+                                        float* logits, float* lse, int32_t* idx, float* gate,
+                                        const float* noise, double sigma, hipStream_t st) {
+#define MOE_ROUTER_EP(EPV) \
+  return launch_router_ep<EPV>(x, xt, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
+  if (E <= 8) MOE_ROUTER_EP(8);
+  if (E <= 16) MOE_ROUTER_EP(16);
+  if (E <= 32) MOE_ROUTER_EP(32);
+  if (E <= 64) MOE_ROUTER_EP(64);
+  if (E <= 128) MOE_ROUTER_EP(128);
+  MOE_ROUTER_EP(256);
+#undef MOE_ROUTER_EP
 }
 
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
-                         float* lse, int32_t* idx, float* gate, void* ws, hipStream_t st) {
+                         float* lse, int32_t* idx, float* gate, const float* noise, double sigma,
+                         void* ws, hipStream_t st) {
   if (router_uses_mfma(xbf16, d, E)) {
-    if (E <= 64) return launch_router_mfma<64>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
-    if (E <= 128) return launch_router_mfma<128>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
-    return launch_router_mfma<256>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, ws, st);
+#define MOE_ROUTER_MFMA(EPV) \
+  return launch_router_mfma<EPV>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, ws, st)
+    if (E <= 64) MOE_ROUTER_MFMA(64);
+    if (E <= 128) MOE_ROUTER_MFMA(128);
+    MOE_ROUTER_MFMA(256);
+#undef MOE_ROUTER_MFMA
   }
   // K-split when W_g fits in 64 KB of LDS and E <= 64
   if ((int64_t)E * d * 4 <= 65536 && E <= 64) {
-    if (E <= 8) return launch_router_ksplit<8>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-    if (E <= 16) return launch_router_ksplit<16>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-    if (E <= 32) return launch_router_ksplit<32>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-    return launch_router_ksplit<64>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
+#define MOE_ROUTER_KS(EPV) \
+  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
+    if (E <= 8) MOE_ROUTER_KS(8);
+    if (E <= 16) MOE_ROUTER_KS(16);
+    if (E <= 32) MOE_ROUTER_KS(32);
+    MOE_ROUTER_KS(64);
+#undef MOE_ROUTER_KS
   }
-  if (E <= 8) return launch_router_ep<8>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-  if (E <= 16) return launch_router_ep<16>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-  if (E <= 32) return launch_router_ep<32>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-  if (E <= 64) return launch_router_ep<64>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-  if (E <= 128) return launch_router_ep<128>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
-  return launch_router_ep<256>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, st);
+  return launch_router_e_split(x, xbf16 ? XT_BF16 : XT_F32, T, d, Wg, bg, bsel, E, k, logits, lse, idx,
+                               gate, noise, sigma, st);
+}
+
+template <int HP>
+static hipError_t launch_mlp_hidden(const void* x, bool xbf16, int64_t T, int d, const float* gW1,
+                                    const float* gb1, int H, double* hidden, hipStream_t st) {
+  using C = RouterCfg<HP>;
+  const dim3 grid((unsigned)((T + C::BT - 1) / C::BT));
+  if (xbf16)
+    hipLaunchKernelGGL((mlp_gate_hidden_kernel<HP, XT_BF16>), grid, dim3(C::NT), 0, st, x, T, d, gW1, gb1, H,
+                       hidden);
+  else
+    hipLaunchKernelGGL((mlp_gate_hidden_kernel<HP, XT_F32>), grid, dim3(C::NT), 0, st, x, T, d, gW1, gb1, H,
+                       hidden);
+  return hipGetLastError();
+}
+
+size_t mlp_router_ws_bytes(int64_t T, int H) { return align256((size_t)T * (size_t)H * sizeof(double)); }
+
+hipError_t launch_mlp_router(const void* x, bool xbf16, int64_t T, int d, const float* gW1,
+                             const float* gb1, int H, const float* gW2, const float* gb2,
+                             const float* bsel, int E, int k, float* logits, float* lse, int32_t* idx,
+                             float* gate, const float* noise, double sigma, void* ws, hipStream_t st) {
+  double* hidden = (double*)ws;
+  hipError_t e;
+  if (H <= 8) e = launch_mlp_hidden<8>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  else if (H <= 16) e = launch_mlp_hidden<16>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  else if (H <= 32) e = launch_mlp_hidden<32>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  else if (H <= 64) e = launch_mlp_hidden<64>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  else if (H <= 128) e = launch_mlp_hidden<128>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  else e = launch_mlp_hidden<256>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
+  if (e != hipSuccess) return e;
+  return launch_router_e_split(hidden, XT_F64, T, H, gW2, gb2, bsel, E, k, logits, lse, idx, gate, noise,
+                               sigma, st);
 }
 
 }  // namespace moe

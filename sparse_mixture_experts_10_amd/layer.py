@@ -68,12 +68,16 @@ class MoELayer:
     reads token rows of x through row_token; False materialises x_disp first.
     fused_route: True (default, with gather_rows) takes router, dispatch and
     statistics in one moe_route call; False makes the three calls separately.
+    noise, noise_std: noisy top-k, noise [T, E] fp32 standard-normal draws.
+    mlp_gate: (gW1 [H, d], gb1 [H], gW2 [E, H], gb2 [E]) fp32 to route with the
+    MLP gate instead of W_g / b_g (always the separate calls).
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
-                 gather_rows: bool = True, fused_route: bool = True):
+                 gather_rows: bool = True, fused_route: bool = True, noise=None, noise_std: float = 0.0,
+                 mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
@@ -81,7 +85,9 @@ class MoELayer:
         self.cf = None if capacity_factor is None else Fraction(capacity_factor)
         self.alpha, self.beta, self.credit = alpha, beta, credit
         self.gather_rows = gather_rows
-        self.fused = fused_route and gather_rows
+        self.noise, self.noise_std = noise, float(noise_std)
+        self.mlp_gate = mlp_gate
+        self.fused = fused_route and gather_rows and mlp_gate is None
         self.E, self.F, self.d = W1.shape
         self.dtype = W1.dtype
         self.device = W1.device
@@ -111,7 +117,9 @@ class MoELayer:
             y=e(T, d), f=e(E, dtype=f32), P=e(E, dtype=f32), losses=e(3, dtype=f32),
             credit=e(T, k, dtype=f32) if self.credit else None,
             mean_credit=e(E, dtype=f32) if self.credit else None,
-            ws_router=_ws(api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E), dev),
+            ws_router=_ws(api.moe_workspace_bytes(api.OP_MLP_ROUTER, T=T, F=self.mlp_gate[0].shape[0])
+                          if self.mlp_gate is not None else api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E),
+                          dev),
             ws_dispatch=_ws(api.moe_workspace_bytes(api.OP_DISPATCH, T=T, E=E), dev),
             ws_ffn=_ws(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dev) if self.credit else None,
             ws_stats=_ws(api.moe_workspace_bytes(api.OP_STATS, T=T, E=E, k=k), dev),
@@ -149,11 +157,17 @@ class MoELayer:
         o.x = x
         api.moe_route(x, self.W_g, self.b_g, self.b_sel, self.k, o.capacity, self.alpha, self.beta,
                       o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, o.expert_offset, o.slot,
-                      o.row, o.row_token, o.f, o.P, o.losses, o.ws_route, stream)
+                      o.row, o.row_token, o.f, o.P, o.losses, o.ws_route, stream, noise=self.noise,
+                      noise_std=self.noise_std)
 
     def router(self, x, o: MoEOutputs, stream=None) -> None:
+        if self.mlp_gate is not None:
+            gW1, gb1, gW2, gb2 = self.mlp_gate
+            api.moe_mlp_router_topk(x, gW1, gb1, gW2, gb2, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
+                                    o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std)
+            return
         api.moe_router_topk(x, self.W_g, self.b_g, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
-                            o.topk_gate, o.ws_router, stream)
+                            o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std)
 
     def dispatch(self, x, o: MoEOutputs, stream=None) -> None:
         o.x = x

@@ -42,10 +42,12 @@ def build_layer(inp: synth.Inputs, device="cuda", gather_rows=True, fused_route=
     w = inp.workload
     t = to_torch(inp, device)
     shared = (t["sW1"], t["sb1"], t["sW2"], t["sb2"]) if w.n_shared else None
+    gate = (t["gW1"], t["gb1"], t["gW2"], t["gb2"]) if w.mlp_gate else None
     layer = MoELayer(t["W_g"], t["W1"], t["b1"], t["W2"], t["b2"], k=w.k, act=w.act,
                      capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
                      alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=gather_rows,
-                     fused_route=fused_route)
+                     fused_route=fused_route, noise=t["noise"], noise_std=w.router_noise or 0.0,
+                     mlp_gate=gate)
     return layer, t["x"]
 
 

@@ -83,8 +83,8 @@ def _router(**kw):
     a = dict(x=FAKE, dt=1, T=16, d=8, W=FAKE, bg=NULL, bs=NULL, E=4, k=2, lg=FAKE, lse=FAKE, idx=FAKE, g=FAKE)
     a.update(kw)
     return _native.load().moe_router_topk(a["x"], a["dt"], a["T"], a["d"], a["W"], a["bg"], a["bs"], a["E"],
-                                          a["k"], a["lg"], a["lse"], a["idx"], a["g"], a.get("ws"),
-                                          a.get("wsb", 0), None)
+                                          a["k"], a.get("nz"), 0.5, a["lg"], a["lse"], a["idx"], a["g"],
+                                          a.get("ws"), a.get("wsb", 0), None)
 
 
 def test_router_validation():
@@ -106,6 +106,27 @@ def test_router_validation():
     assert _router(E=128, d=4096, k=8, ws=FAKE, wsb=16) == WORKSPACE
     assert api.moe_workspace_bytes(api.OP_ROUTER, T=32768, d=4096, E=128) >= 3 * 128 * 4096 * 2 + 32768
     assert api.moe_workspace_bytes(api.OP_ROUTER, T=4096, d=512, E=8) == 0
+
+
+def _mlp_router(**kw):
+    a = dict(x=FAKE, dt=1, T=16, d=8, W1=FAKE, b1=NULL, H=16, W2=FAKE, b2=NULL, bs=NULL, E=4, k=2, lg=FAKE,
+             lse=FAKE, idx=FAKE, g=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return _native.load().moe_mlp_router_topk(a["x"], a["dt"], a["T"], a["d"], a["W1"], a["b1"], a["H"], a["W2"],
+                                              a["b2"], a["bs"], a["E"], a["k"], None, 0.0, a["lg"], a["lse"],
+                                              a["idx"], a["g"], a["ws"], a["wsb"], None)
+
+
+def test_mlp_router_validation():
+    assert _mlp_router(H=12) == INVALID            # hidden width not a multiple of 8
+    assert _mlp_router(H=264) == UNSUPPORTED
+    assert _mlp_router(k=5) == INVALID
+    assert _mlp_router(W1=NULL) == INVALID
+    assert _mlp_router(W2=MIS) == INVALID
+    assert _mlp_router(ws=NULL) == WORKSPACE
+    assert _mlp_router(wsb=100) == WORKSPACE
+    assert _mlp_router(T=0) == OK
+    assert api.moe_workspace_bytes(api.OP_MLP_ROUTER, T=1000, F=128) >= 1000 * 128 * 8
 
 
 def _dispatch(**kw):
@@ -137,7 +158,7 @@ def _route(**kw):
              ws=FAKE, wsb=1 << 20)
     a.update(kw)
     return _native.load().moe_route(a["x"], a["dt"], a["T"], a["d"], a["W"], a["bg"], a["bs"], a["E"], a["k"],
-                                    a["cap"], 0.01, 1e-3, a["lg"], a["lse"], a["idx"], a["g"], a["cnt"],
+                                    None, 0.0, a["cap"], 0.01, 1e-3, a["lg"], a["lse"], a["idx"], a["g"], a["cnt"],
                                     a["off"], a["slot"], a["row"], a["rt"], a["f"], a["P"], a["L"], a["ws"],
                                     a["wsb"], None)
 

@@ -25,6 +25,12 @@ SCALED = {
     "large_credit_s": synth.LARGE_CREDIT.with_(T=1024, d=512, F=384),
     "ragged": synth.DEFAULT.with_(T=1000, d=136, F=72, E=5, k=3, capacity_factor=Fraction(3, 4)),
     "ragged_fp32": synth.TINY.with_(T=333, d=40, F=24, E=7, k=3, act="gelu", capacity_factor=Fraction(7, 10)),
+    # router variants: noisy top-k (on-chip, E-split and MFMA router paths) and the MLP gate
+    "noisy_default": synth.DEFAULT.with_(T=1024, router_noise=1.0),
+    "noisy_e_split": synth.DEFAULT.with_(T=700, d=72, F=64, E=100, k=4, router_noise=0.3, capacity_factor=None),
+    "noisy_mfma": synth.LARGE_CREDIT.with_(T=1024, d=512, F=384, router_noise=0.5),
+    "mlp_gate": synth.DEFAULT.with_(T=1000, d=136, F=72, E=12, k=3, mlp_gate=128, capacity_factor=Fraction(3, 2)),
+    "mlp_gate_noisy_fp32": synth.TINY.with_(T=300, d=40, F=24, E=6, k=2, mlp_gate=32, router_noise=0.2),
 }
 
 
