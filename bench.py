@@ -8,9 +8,10 @@ synthetic inputs already resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload default]
 
 Steps are timed as K replays of one HIP graph holding the whole pass.  Per-call
-durations come from HIP events recorded around each call on the stream the
-kernels run on (torch's current stream, which every call is given), with the
-queue kept full so the events measure the GPU and not host launch latency.  The dominant
+durations come from HIP events on the stream the kernels run on (torch's
+current stream, which every call is given) around K replays of a graph holding
+R back-to-back launches of that one call, with the queue kept full so the
+events measure the GPU and not host launch latency.  The dominant
 kernel is the bf16 grouped GEMM (two launches per step: expert up and expert
 down); its roofline figure uses the algorithmic FLOPs of one launch,
 2 * rows * d * F for the kept rows, over the measured average launch time.
@@ -176,32 +177,35 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / K
 
-    # Per call: events around each call of K eager steps, queue pre-filled the same way.
-    evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(K)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 600e-6 * K))
-    for s in range(K):
-        evs[s][0].record()
-        for i, (_, fn) in enumerate(calls):
-            fn()
-            evs[s][i + 1].record()
-    torch.cuda.synchronize()
-    per_call = {name: float(np.median([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)])) * 1e3
-                for i, (name, _) in enumerate(calls)}   # microseconds
+    # Per call: each call captured R times back to back in a graph of its own
+    # and replayed K times between two events (queue pre-filled the same way),
+    # so the figure is the call's GPU time per launch without host gaps.
+    R = 8
+
+    def time_call(fn, budget_us):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(R):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        torch.cuda._sleep(int(2.4e9 * budget_us * 1e-6 * R * K))
+        a.record()
+        for _ in range(K):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (K * R)     # microseconds per call
+
+    budget = ms_step * 1e3
+    per_call = {name: time_call(fn, budget) for name, fn in calls}
     ms_step_eager = sum(per_call.values()) / 1e3
 
     # The dispatch on its own (the index-only moe_dispatch call, which the fused
     # routing pass contains), timed the same way, for the dispatch GB/s figure.
     if "dispatch" not in per_call:
-        dev = [(ev(), ev()) for _ in range(K)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 30e-6 * K))
-        for a, b in dev:
-            a.record()
-            layer.dispatch(x, o)
-            b.record()
-        torch.cuda.synchronize()
-        per_call_dispatch = float(np.median([a.elapsed_time(b) for a, b in dev])) * 1e3
+        per_call_dispatch = time_call(lambda: layer.dispatch(x, o), budget)
     else:
         per_call_dispatch = per_call["dispatch"]
 
@@ -254,7 +258,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "ms_per_step_calls": ms_step_eager,
+        "ms_per_step_calls": ms_step_eager,     # sum of the per-call times
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
