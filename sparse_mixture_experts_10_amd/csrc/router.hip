@@ -330,6 +330,7 @@ __device__ __forceinline__ void rs_halve(const double (&v)[N], double (&w)[N / 2
 
 constexpr int KS_LPT = 16;    // lanes per token
 constexpr int KS_TPB = 16;    // tokens per block (256 threads)
+constexpr int KS_XV = 16;     // x vectors per lane: d <= 16 * 16 * 8 (bf16) or 16 * 16 * 4 (fp32)
 
 template <int EP, bool XBF16>
 __global__ __launch_bounds__(256) void router_ksplit_kernel(
@@ -342,6 +343,19 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
   const int lane = tid & (KS_LPT - 1);
   const int64_t t = (int64_t)blockIdx.x * KS_TPB + tid / KS_LPT;
 
+  // this lane's slice of the token row, loaded before the W_g fill so both
+  // loads are in flight together (d <= kKsMaxD: at most KS_XV vectors a lane)
+  constexpr int XW = XBF16 ? 8 : 4;   // elements per 16-byte vector
+  vec16 xr[KS_XV];
+#pragma unroll
+  for (int it = 0; it < KS_XV; ++it) {
+    const int col = (lane + KS_LPT * it) * XW;
+    if (t < T && col < d) {
+      xr[it] = XBF16 ? *(const vec16*)((const bf16_t*)xv + t * (int64_t)d + col)
+                     : *(const vec16*)((const float*)xv + t * (int64_t)d + col);
+    }
+  }
+
   const int nv4 = E * d / 4;
   for (int v = tid; v < nv4; v += 256) ((float4*)wsm)[v] = ((const float4*)Wg)[v];
   __syncthreads();
@@ -350,42 +364,33 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
 #pragma unroll
   for (int e = 0; e < EP; ++e) acc[e] = 0.0;
   if (t < T) {
-    if (XBF16) {
-      const bf16_t* x = (const bf16_t*)xv + t * (int64_t)d;
-      for (int col = lane * 8; col < d; col += KS_LPT * 8) {
+#pragma unroll
+    for (int it = 0; it < KS_XV; ++it) {
+      const int col = (lane + KS_LPT * it) * XW;
+      if (col < d) {
         float f[8];
-        unpack_bf16x8(*(const vec16*)(x + col), f);
+        if (XBF16) {
+          unpack_bf16x8(xr[it], f);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(xr[it].w[q]);
+        }
 #pragma unroll
         for (int e = 0; e < EP; ++e) {
           if (e < E) {
             const float4 w0 = *(const float4*)(wsm + e * d + col);
-            const float4 w1 = *(const float4*)(wsm + e * d + col + 4);
             double a = acc[e];
             a = fma((double)f[0], (double)w0.x, a);
             a = fma((double)f[1], (double)w0.y, a);
             a = fma((double)f[2], (double)w0.z, a);
             a = fma((double)f[3], (double)w0.w, a);
-            a = fma((double)f[4], (double)w1.x, a);
-            a = fma((double)f[5], (double)w1.y, a);
-            a = fma((double)f[6], (double)w1.z, a);
-            a = fma((double)f[7], (double)w1.w, a);
-            acc[e] = a;
-          }
-        }
-      }
-    } else {
-      const float* x = (const float*)xv + t * (int64_t)d;
-      for (int col = lane * 4; col < d; col += KS_LPT * 4) {
-        const float4 q = *(const float4*)(x + col);
-#pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          if (e < E) {
-            const float4 w0 = *(const float4*)(wsm + e * d + col);
-            double a = acc[e];
-            a = fma((double)q.x, (double)w0.x, a);
-            a = fma((double)q.y, (double)w0.y, a);
-            a = fma((double)q.z, (double)w0.z, a);
-            a = fma((double)q.w, (double)w0.w, a);
+            if (XBF16) {
+              const float4 w1 = *(const float4*)(wsm + e * d + col + 4);
+              a = fma((double)f[4], (double)w1.x, a);
+              a = fma((double)f[5], (double)w1.y, a);
+              a = fma((double)f[6], (double)w1.z, a);
+              a = fma((double)f[7], (double)w1.w, a);
+            }
             acc[e] = a;
           }
         }
@@ -646,8 +651,8 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
     MOE_ROUTER_MFMA(256);
 #undef MOE_ROUTER_MFMA
   }
-  // K-split when W_g fits in 64 KB of LDS and E <= 64
-  if ((int64_t)E * d * 4 <= 65536 && E <= 64) {
+  // K-split when W_g fits in 64 KB of LDS, E <= 64 and the row fits KS_XV vectors a lane
+  if ((int64_t)E * d * 4 <= 65536 && E <= 64 && d <= KS_LPT * KS_XV * (xbf16 ? 8 : 4)) {
 #define MOE_ROUTER_KS(EPV) \
   return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
     if (E <= 8) MOE_ROUTER_KS(8);

@@ -71,13 +71,15 @@ class MoELayer:
     noise, noise_std: noisy top-k, noise [T, E] fp32 standard-normal draws.
     mlp_gate: (gW1 [H, d], gb1 [H], gW2 [E, H], gb2 [E]) fp32 to route with the
     MLP gate instead of W_g / b_g (always the separate calls).
+    overlap_shared: run the shared experts on a side stream, concurrently with
+    the routed path (forward only; calls() lists every call in order).
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
                  gather_rows: bool = True, fused_route: bool = True, noise=None, noise_std: float = 0.0,
-                 mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None):
+                 mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
@@ -86,6 +88,8 @@ class MoELayer:
         self.alpha, self.beta, self.credit = alpha, beta, credit
         self.gather_rows = gather_rows
         self.noise, self.noise_std = noise, float(noise_std)
+        self.overlap_shared = overlap_shared
+        self._side = None
         self.mlp_gate = mlp_gate
         self.fused = fused_route and gather_rows and mlp_gate is None
         self.E, self.F, self.d = W1.shape
@@ -131,9 +135,32 @@ class MoELayer:
         o = self.allocate(T) if out is None else out
         if o.T != T:
             raise ValueError("output buffers were allocated for another batch size")
-        for _, call in self.calls(x, o, stream):
+        if self.shared is None or not self.overlap_shared:
+            for _, call in self.calls(x, o, stream):
+                call()
+            return o
+        # The shared experts need only x: they run on a side stream while the
+        # routed path runs, and the combine waits for them.
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        side = self._side_stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        self.shared_experts(x, o, side)
+        joined = torch.cuda.Event()
+        joined.record(side)
+        for name, call in self.calls(x, o, stream):
+            if name == "shared":
+                continue
+            if name == "combine":
+                main.wait_event(joined)
             call()
         return o
+
+    def _side_stream(self):
+        if self._side is None:
+            self._side = torch.cuda.Stream(self.device)   # default priority
+        return self._side
 
     def calls(self, x, o: MoEOutputs, stream=None):
         """The ABI calls of one forward pass, in order, as (name, thunk) pairs."""
