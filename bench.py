@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # Sources that decide which grouped-GEMM kernel runs and what it does: HBM byte
 # counters recorded for an older version of them are not reported.
-GEMM_SOURCES = ["gemm_bf16_v2.hip", "gemm_tiles.h", "grouped_gemm.hip", "internal.h", "common.h"]
+GEMM_SOURCES = ["gemm_bf16_v2.hip", "gemm_tiles.h", "grouped_gemm.hip", "gemm_args.h", "common.h"]
 COUNTER_PREFIX = "traffic-json: "
 
 WORKLOADS = {
