@@ -73,6 +73,15 @@ __device__ __forceinline__ float apply_act(int act, float z) {
   return swish(z);
 }
 
+// Compile-time activation (-1: none), for epilogues with no per-element branch.
+template <int ACT>
+__device__ __forceinline__ float act_static(float z) {
+  if constexpr (ACT == ACT_RELU) return fmaxf(z, 0.0f);
+  else if constexpr (ACT == ACT_GELU) return gelu_erf(z);
+  else if constexpr (ACT == ACT_SWISH) return swish(z);
+  else return z;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));

@@ -73,7 +73,8 @@ struct V2 {
 
 // One LDS array per stage: distinct objects let the compiler see that reading
 // one stage does not alias the loads in flight into the others.
-template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG>
+// ACT: the epilogue activation, fixed at compile time (-1: none; p.act must match).
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG, int ACT>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(GemmArgs p) {
   using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG>;
   constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
           const int m = wm * C::WM + i * 16 + fc * 4 + r;
           const int n = n0 + wn * C::WN + j * 16 + fr;
           float v = acc[i][j][r] + bcol[j];
-          if (p.act >= 0) v = apply_act(p.act, v);
+          v = act_static<ACT>(v);
           if (m < tl.M && n < N) Cf[(tl.row0 + m) * (int64_t)N + n] = v;
         }
     return;
@@ -242,9 +243,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = acc[i][j][r] + bcol[j];
-        if (p.act >= 0) v = apply_act(p.act, v);
-        if (ncol_ok[j]) rs[r] += v * v;
+        const float v = act_static<ACT>(acc[i][j][r] + bcol[j]);
+        if (want_sq && ncol_ok[j]) rs[r] += v * v;
         Cs[(wm * 16 + fc * 4 + r) * C::LDC + wn * C::WN + j * 16 + fr] = f32_to_bf16(v);
       }
     }
@@ -286,10 +286,22 @@ static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
   const int64_t mt = (rows + BM - 1) / BM + (a.group_offset ? a.G : 0);
   const dim3 grid((unsigned)grid_blocks(mt, (a.N + BN - 1) / BN));
   const dim3 block(64 * WGM * WGN);
-  if (a.S > 1)
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, false>), grid, block, 0, st, a);
+#define MOE_V2_LAUNCH(SEGV, ACTV) \
+  hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, SEGV, ACTV>), grid, block, 0, st, a)
+#define MOE_V2_BY_ACT(SEGV)                                  \
+  switch (a.act) {                                           \
+    case ACT_RELU: MOE_V2_LAUNCH(SEGV, ACT_RELU); break;     \
+    case ACT_GELU: MOE_V2_LAUNCH(SEGV, ACT_GELU); break;     \
+    case ACT_SWISH: MOE_V2_LAUNCH(SEGV, ACT_SWISH); break;   \
+    default: MOE_V2_LAUNCH(SEGV, -1); break;                 \
+  }
+  if (a.S > 1) {
+    MOE_V2_BY_ACT(true);
+  } else {
+    MOE_V2_BY_ACT(false);
+  }
+#undef MOE_V2_BY_ACT
+#undef MOE_V2_LAUNCH
   return hipGetLastError();
 }
 
