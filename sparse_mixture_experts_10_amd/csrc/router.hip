@@ -41,38 +41,85 @@ struct RouterCfg {
   static constexpr int KC = (EP >= 256) ? 32 : 64;          // d-chunk staged in LDS
 };
 
-template <int NXE>
-__device__ __forceinline__ double group_max(double v) {
-#pragma unroll
-  for (int m = 1; m < NXE; m <<= 1) v = fmax(v, __shfl_xor(v, m, 64));
-  return v;
+// Exchange with lane ^ M.  Inside a 16-lane row this is DPP (quad permutes for
+// M = 1, 2; row rotates for M = 4, 8), a plain VALU move; M >= 16 goes
+// through ds_bpermute.  Every lane must be active.
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    // rotate the row by 4 one way or the other: each lane keeps the rotation
+    // that brings it lane ^ 4 (decided from the lane ids themselves)
+    const int lid = (int)__lane_id();
+    const int a = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    const int b = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, false);  // row_ror:12
+    const int src_a = __builtin_amdgcn_update_dpp(0, lid, 0x124, 0xF, 0xF, false);
+    return src_a == (lid ^ 4) ? a : b;
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8 (= lane ^ 8)
+  } else {
+    return __shfl_xor(v, M, 64);
+  }
 }
 
+template <int M>
+__device__ __forceinline__ double xor_lane_d(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = xor_lane<M>((int)(u & 0xffffffffll));
+  const int hi = xor_lane<M>((int)(u >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+template <int M>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __int_as_float(xor_lane<M>(__float_as_int(v)));
+}
+
+// Reductions over NXE consecutive lanes, partners at lane ^ 1, ^ 2, ^ 4, ...
+// in that order (every lane ends with the same value).
 template <int NXE>
-__device__ __forceinline__ double group_sum(double v) {
-#pragma unroll
-  for (int m = 1; m < NXE; m <<= 1) v += __shfl_xor(v, m, 64);
+__device__ __forceinline__ double group_max(double v) {
+  if constexpr (NXE > 1) v = fmax(v, xor_lane_d<1>(v));
+  if constexpr (NXE > 2) v = fmax(v, xor_lane_d<2>(v));
+  if constexpr (NXE > 4) v = fmax(v, xor_lane_d<4>(v));
+  if constexpr (NXE > 8) v = fmax(v, xor_lane_d<8>(v));
+  if constexpr (NXE > 16) v = fmax(v, xor_lane_d<16>(v));
+  if constexpr (NXE > 32) v = fmax(v, xor_lane_d<32>(v));
   return v;
 }
 
 template <int NXE>
 __device__ __forceinline__ float group_sumf(float v) {
-#pragma unroll
-  for (int m = 1; m < NXE; m <<= 1) v += __shfl_xor(v, m, 64);
+  if constexpr (NXE > 1) v += xor_lane_f<1>(v);
+  if constexpr (NXE > 2) v += xor_lane_f<2>(v);
+  if constexpr (NXE > 4) v += xor_lane_f<4>(v);
+  if constexpr (NXE > 8) v += xor_lane_f<8>(v);
+  if constexpr (NXE > 16) v += xor_lane_f<16>(v);
+  if constexpr (NXE > 32) v += xor_lane_f<32>(v);
   return v;
 }
 
-// (score desc, index asc) argmax across the NXE lanes of a token; carries h.
+// One step of the (score desc, index asc) argmax across lanes; carries x.
+template <int M>
+__device__ __forceinline__ void argmax_step(double& s, int& e, float& x) {
+  const double so = xor_lane_d<M>(s);
+  const int eo = xor_lane<M>(e);
+  const float xo = xor_lane_f<M>(x);
+  const bool take = (so > s) || (so == s && eo < e);
+  if (take) { s = so; e = eo; x = xo; }
+}
+
 template <int NXE>
-__device__ __forceinline__ void group_argmax(double& s, int& e, double& h) {
-#pragma unroll
-  for (int m = 1; m < NXE; m <<= 1) {
-    double so = __shfl_xor(s, m, 64);
-    int eo = __shfl_xor(e, m, 64);
-    double ho = __shfl_xor(h, m, 64);
-    bool take = (so > s) || (so == s && eo < e);
-    if (take) { s = so; e = eo; h = ho; }
-  }
+__device__ __forceinline__ void group_argmax(double& s, int& e, float& x) {
+  if constexpr (NXE > 1) argmax_step<1>(s, e, x);
+  if constexpr (NXE > 2) argmax_step<2>(s, e, x);
+  if constexpr (NXE > 4) argmax_step<4>(s, e, x);
+  if constexpr (NXE > 8) argmax_step<8>(s, e, x);
+  if constexpr (NXE > 16) argmax_step<16>(s, e, x);
+  if constexpr (NXE > 32) argmax_step<32>(s, e, x);
 }
 
 // Per-token epilogue.  The NXE lanes of a token hold its fp64 dot products
@@ -85,6 +132,7 @@ __device__ __forceinline__ void group_argmax(double& s, int& e, double& h) {
 // consecutive scores among the k + 1 highest (k when k = E) are closer than
 // flag_rel * max(1, |score|): the selected set or its listed order could then
 // change within the logits' rounding error.
+// Every lane of the wave must be active (the cross-lane steps use DPP).
 template <int TE, int NXE>
 __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, int64_t t, bool live,
                                                int E, int k, const float* __restrict__ bg,
@@ -101,16 +149,22 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
   for (int j = 0; j < TE; ++j) {
     const int e = eg + NXE * j;
     const bool ok = e < E;
-    double hv = acc[j] + (bg != nullptr ? (double)bg[e] : 0.0);
+    double hv = acc[j] + (bg != nullptr && ok ? (double)bg[e] : 0.0);
     if (noise != nullptr && live && ok) hv += sigma * (double)noise[t * E + e];
     h[j] = ok ? hv : NEG;
     s[j] = ok ? h[j] + (bsel != nullptr ? (double)bsel[e] : 0.0) : NEG;
     m = fmax(m, h[j]);
   }
   m = group_max<NXE>(m);
+  // exp(h - m) in fp32 for every expert; the lse uses their sum, the gates
+  // the selected ones
+  float ex[TE];
   float se = 0.f;
 #pragma unroll
-  for (int j = 0; j < TE; ++j) se += (eg + NXE * j < E) ? expf((float)(h[j] - m)) : 0.f;
+  for (int j = 0; j < TE; ++j) {
+    ex[j] = (eg + NXE * j < E) ? expf((float)(h[j] - m)) : 0.f;
+    se += ex[j];
+  }
   se = group_sumf<NXE>(se);
   if (live) {
 #pragma unroll
@@ -120,36 +174,48 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
     }
     if (eg == 0) lse_out[t] = (float)(m + (double)logf(se));
   }
-  // two passes of k argmax rounds: the first sums the selected exp(h - m),
-  // the second writes indices and gates in selection order
+  // k argmax rounds in selection order (one more for the near-tie flag); the
+  // lane owning a selected expert records its round, and once the sum of the
+  // selected exp(h - m) is known writes that expert's index and gate
   float gsum = 0.f;
   bool near = false;
   double prev = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    uint32_t taken = 0;
-    const int rounds = (pass == 0 && flag_rel > 0.0 && k < E) ? k + 1 : k;
-    for (int r = 0; r < rounds; ++r) {
-      double bs = NEG, bh = 0.0;
-      int be = 0x7fffffff;
+  uint32_t taken = 0;
+  int rank[TE];
 #pragma unroll
-      for (int j = 0; j < TE; ++j) {
-        const int e = eg + NXE * j;
-        const bool ok = (e < E) && !((taken >> j) & 1u);
-        if (ok && (s[j] > bs || (s[j] == bs && e < be))) { bs = s[j]; be = e; bh = h[j]; }
-      }
-      group_argmax<NXE>(bs, be, bh);
-      if (pass == 0 && flag_rel > 0.0) {
-        if (r > 0 && prev - bs < flag_rel * fmax(1.0, fabs(prev))) near = true;
-        prev = bs;
-      }
-      if (r == k) break;  // the (k+1)-th score only feeds the flag
-      if (be % NXE == eg) taken |= 1u << (be / NXE);
-      const float ex = expf((float)(bh - m));
-      if (pass == 0) {
-        gsum += ex;
-      } else if (live && eg == 0) {
-        topk_idx[t * k + r] = be;
-        topk_gate[t * k + r] = ex / gsum;
+  for (int j = 0; j < TE; ++j) rank[j] = 0;
+  const int rounds = (flag_rel > 0.0 && k < E) ? k + 1 : k;
+  for (int r = 0; r < rounds; ++r) {
+    double bs = NEG;
+    int be = 0x7fffffff;
+    float bx = 0.f;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = eg + NXE * j;
+      const bool ok = (e < E) && !((taken >> j) & 1u);
+      if (ok && (s[j] > bs || (s[j] == bs && e < be))) { bs = s[j]; be = e; bx = ex[j]; }
+    }
+    group_argmax<NXE>(bs, be, bx);
+    if (flag_rel > 0.0) {
+      if (r > 0 && prev - bs < flag_rel * fmax(1.0, fabs(prev))) near = true;
+      prev = bs;
+    }
+    if (r == k) break;  // the (k+1)-th score only feeds the flag
+    if (be % NXE == eg) {
+      const int jb = be / NXE;
+      taken |= 1u << jb;
+#pragma unroll
+      for (int j = 0; j < TE; ++j)
+        if (j == jb) rank[j] = r;
+    }
+    gsum += bx;
+  }
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      if ((taken >> j) & 1u) {
+        topk_idx[t * k + rank[j]] = eg + NXE * j;
+        topk_gate[t * k + rank[j]] = ex[j] / gsum;
       }
     }
   }
@@ -324,13 +390,34 @@ __device__ __forceinline__ void rs_halve(const double (&v)[N], double (&w)[N / 2
     const int i0 = (q / O) * 2 * O + q % O;
     const double keep = hi ? v[i0 + O] : v[i0];
     const double send = hi ? v[i0] : v[i0 + O];
-    w[q] = keep + __shfl_xor(send, O, 64);
+    w[q] = keep + xor_lane_d<O>(send);
   }
 }
 
 constexpr int KS_LPT = 16;    // lanes per token
 constexpr int KS_TPB = 16;    // tokens per block (256 threads)
 constexpr int KS_XV = 16;     // x vectors per lane: d <= 16 * 16 * 8 (bf16) or 16 * 16 * 4 (fp32)
+constexpr int KS_FB = 4;      // W_g float4 loads a thread has in flight during the LDS fill
+
+// LDS layout of W_g in the K-split kernel.  A token's 16 lanes read the row in
+// chunks of CH = 16 * XW columns, lane l taking columns l * XW .. l * XW + XW - 1
+// of each chunk (XW = 8 for bf16 x, 4 for fp32 x).  Inside a chunk the float4
+// quarter q of lane l's columns sits at float4 index q * 16 + l, so one
+// ds_read_b128 of the 16 lanes covers 256 contiguous bytes (no bank
+// conflicts).  Each expert row is padded to whole chunks.
+__host__ __device__ constexpr int ks_chunk_cols(bool xbf16) { return KS_LPT * (xbf16 ? 8 : 4); }
+
+__host__ __device__ inline int ks_row_float4(int d, bool xbf16) {
+  const int ch = ks_chunk_cols(xbf16);
+  return (d + ch - 1) / ch * (ch / 4);
+}
+
+// Experts are padded to EP rows of zeros so the inner loop needs no expert guard.
+static int ks_expert_rows(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
+
+static size_t ks_lds_bytes(int E, int d, bool xbf16) {
+  return (size_t)ks_expert_rows(E) * ks_row_float4(d, xbf16) * sizeof(float4);
+}
 
 template <int EP, bool XBF16>
 __global__ __launch_bounds__(256) void router_ksplit_kernel(
@@ -338,61 +425,96 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
-  extern __shared__ float wsm[];  // W_g [E][d], fp32
+  extern __shared__ float4 wsm[];  // W_g, fp32, in the chunked layout above
+  constexpr int XW = XBF16 ? 8 : 4;   // elements per 16-byte x vector
+  constexpr int CH = KS_LPT * XW;     // columns per chunk
+  constexpr int CH4 = CH / 4;         // float4 per chunk
+  // chunks a 64 KB W_g copy of EP rows can hold: the most x vectors a lane needs
+  constexpr int XV = (16384 / (EP * CH)) < KS_XV ? 16384 / (EP * CH) : KS_XV;
+  static_assert(XV >= 1, "W_g rows do not fit the LDS budget");
   const int tid = threadIdx.x;
   const int lane = tid & (KS_LPT - 1);
   const int64_t t = (int64_t)blockIdx.x * KS_TPB + tid / KS_LPT;
+  const int row4 = ks_row_float4(d, XBF16);
 
   // this lane's slice of the token row, loaded before the W_g fill so both
-  // loads are in flight together (d <= kKsMaxD: at most KS_XV vectors a lane)
-  constexpr int XW = XBF16 ? 8 : 4;   // elements per 16-byte vector
-  vec16 xr[KS_XV];
+  // loads are in flight together (at most XV vectors a lane); columns past
+  // d (and rows past T) are zero
+  const int nit = (d + CH - 1) / CH;
+  vec16 xr[XV];
 #pragma unroll
-  for (int it = 0; it < KS_XV; ++it) {
-    const int col = (lane + KS_LPT * it) * XW;
+  for (int it = 0; it < XV; ++it) {
+    const int col = it * CH + lane * XW;
+    xr[it] = vec16{{0u, 0u, 0u, 0u}};
     if (t < T && col < d) {
       xr[it] = XBF16 ? *(const vec16*)((const bf16_t*)xv + t * (int64_t)d + col)
                      : *(const vec16*)((const float*)xv + t * (int64_t)d + col);
     }
   }
 
-  const int nv4 = E * d / 4;
-  for (int v = tid; v < nv4; v += 256) ((float4*)wsm)[v] = ((const float4*)Wg)[v];
+  // W_g -> LDS, EP rows (rows past E and columns past d are zero): KS_FB loads
+  // in flight per thread, then their stores
+  const int nv4 = EP * row4;
+  for (int v0 = 0; v0 < nv4; v0 += 256 * KS_FB) {
+    float4 q[KS_FB];
+#pragma unroll
+    for (int i = 0; i < KS_FB; ++i) {
+      const int v = v0 + tid + 256 * i;
+      q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (v < nv4) {
+        const int e = v / row4, r = v - e * row4;
+        const int c = r / CH4, w = r - c * CH4;
+        const int col = c * CH + (w & 15) * XW + (w >> 4) * 4;
+        if (e < E && col < d) q[i] = *(const float4*)(Wg + (int64_t)e * d + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KS_FB; ++i) {
+      const int v = v0 + tid + 256 * i;
+      if (v < nv4) wsm[v] = q[i];
+    }
+  }
   __syncthreads();
 
+  // no expert or column guards: the padding is zero (nit is uniform)
   double acc[EP];
 #pragma unroll
   for (int e = 0; e < EP; ++e) acc[e] = 0.0;
-  if (t < T) {
 #pragma unroll
-    for (int it = 0; it < KS_XV; ++it) {
-      const int col = (lane + KS_LPT * it) * XW;
-      if (col < d) {
-        float f[8];
-        if (XBF16) {
-          unpack_bf16x8(xr[it], f);
-        } else {
+  for (int it = 0; it < XV; ++it) {
+    if (it < nit) {
+      double f[XW];
+      if constexpr (XBF16) {
+        float g[8];
+        unpack_bf16x8(xr[it], g);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(xr[it].w[q]);
-        }
+        for (int q = 0; q < 8; ++q) f[q] = (double)g[q];
+      } else {
 #pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          if (e < E) {
-            const float4 w0 = *(const float4*)(wsm + e * d + col);
-            double a = acc[e];
-            a = fma((double)f[0], (double)w0.x, a);
-            a = fma((double)f[1], (double)w0.y, a);
-            a = fma((double)f[2], (double)w0.z, a);
-            a = fma((double)f[3], (double)w0.w, a);
-            if (XBF16) {
-              const float4 w1 = *(const float4*)(wsm + e * d + col + 4);
-              a = fma((double)f[4], (double)w1.x, a);
-              a = fma((double)f[5], (double)w1.y, a);
-              a = fma((double)f[6], (double)w1.z, a);
-              a = fma((double)f[7], (double)w1.w, a);
-            }
-            acc[e] = a;
-          }
+        for (int q = 0; q < 4; ++q) f[q] = (double)__uint_as_float(xr[it].w[q]);
+      }
+      // all of this chunk's W_g quarters first, then one column at a time
+      // across the experts: EP independent fp64 chains, no load-use stall
+      // per expert
+      const float4* wl = wsm + it * CH4 + lane;
+      constexpr int NQ = XW / 4;
+#pragma unroll
+      for (int e0 = 0; e0 < EP; e0 += 8) {
+        float4 w[8][NQ];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int h = 0; h < NQ; ++h) w[e][h] = wl[(e0 + e) * row4 + 16 * h];
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 0], (double)w[e][h].x, acc[e0 + e]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 1], (double)w[e][h].y, acc[e0 + e]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 2], (double)w[e][h].z, acc[e0 + e]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 3], (double)w[e][h].w, acc[e0 + e]);
         }
       }
     }
@@ -405,7 +527,7 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     double a4[4], a2[2];
     double full[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) full[e] = acc[e] + __shfl_xor(acc[e], 8, 64);
+    for (int e = 0; e < 8; ++e) full[e] = acc[e] + xor_lane_d<8>(acc[e]);
     rs_halve<8, 4>(full, a4, lane);
     rs_halve<4, 2>(a4, a2, lane);
     rs_halve<2, 1>(a2, r, lane);
@@ -427,7 +549,7 @@ static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int
                                        float* logits, float* lse, int32_t* idx, float* gate,
                                        const float* noise, double sigma, hipStream_t st) {
   const dim3 grid((unsigned)((T + KS_TPB - 1) / KS_TPB));
-  const size_t lds = (size_t)E * d * sizeof(float);
+  const size_t lds = ks_lds_bytes(E, d, xbf16);
   if (xbf16)
     hipLaunchKernelGGL((router_ksplit_kernel<EP, true>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
                        bsel, E, k, logits, lse, idx, gate, noise, sigma);
@@ -569,7 +691,7 @@ size_t router_mfma_ws_bytes(int64_t T, int d, int E) {
 }
 
 bool router_uses_mfma(bool xbf16, int d, int E) {
-  return xbf16 && E > 16 && d % 32 == 0 && !((int64_t)E * d * 4 <= 65536 && E <= 64);
+  return xbf16 && E > 16 && d % 32 == 0 && !(ks_lds_bytes(E, d, xbf16) <= 65536 && E <= 64);
 }
 
 template <int EP>
@@ -651,8 +773,9 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
     MOE_ROUTER_MFMA(256);
 #undef MOE_ROUTER_MFMA
   }
-  // K-split when W_g fits in 64 KB of LDS, E <= 64 and the row fits KS_XV vectors a lane
-  if ((int64_t)E * d * 4 <= 65536 && E <= 64 && d <= KS_LPT * KS_XV * (xbf16 ? 8 : 4)) {
+  // K-split when W_g (EP padded rows) fits in 64 KB of LDS and E <= 64; the LDS bound
+  // also keeps the chunk count within the kernel's x vectors
+  if (ks_lds_bytes(E, d, xbf16) <= 65536 && E <= 64 && d <= KS_XV * ks_chunk_cols(xbf16)) {
 #define MOE_ROUTER_KS(EPV) \
   return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
     if (E <= 8) MOE_ROUTER_KS(8);
