@@ -49,7 +49,17 @@ __device__ __forceinline__ int swz(int r) { return SUB == 1 ? (r >> 1) & 3 : r &
 // reads: the compiler may leave the reads of one slab in flight across the
 // next barrier (it places its own lgkmcnt wait at their first use), and a wave
 // that passes the barrier then refills that slab's stage, racing those reads.
-__device__ __forceinline__ void slab_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Built from builtins, not inline asm: inline asm makes the compiler assume
+// the kernel may use AGPRs and reserve registers for them, which cuts the
+// number of blocks a CU holds.  The signal fences keep the compiler from
+// moving LDS accesses across; lgkmcnt(0) (vmcnt and expcnt left at their
+// maxima) waits for this wave's LDS reads before the barrier.
+__device__ __forceinline__ void slab_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 }  // namespace
 
@@ -61,21 +71,34 @@ struct V2 {
   static constexpr int RB = 64 * SUB;                    // bytes per stage row
   static constexpr int KS = 32 * SUB;                    // K per stage
   static constexpr int RPI = 1024 / RB;                  // rows per load instruction
+  // load instructions per wave per stage: every wave issues the same number
+  // (the vmcnt waits count them).  When BM + BN rows do not split evenly the
+  // surplus instructions (whole RPI-row groups past row BM + BN) load into one
+  // shared 1 KB dummy slot that is never read, so the stages stay unpadded.
+  static constexpr int LPW = (BM + BN + RPI * NW - 1) / (RPI * NW);
+  static constexpr bool PAD = LPW * NW * RPI > BM + BN;
   static constexpr int SLAB = (BM + BN) * RB;            // bytes per stage
-  static constexpr int LPW = (BM + BN) / (RPI * NW);     // load instructions per wave per stage
   static constexpr int SR = 16 * WGM;                    // output rows staged per pass
   static constexpr int LDC = (SR * (BN + 8) * 2 <= SLAB) ? BN + 8 : BN;  // staged row (bf16)
   static_assert(SUB == 1 || SUB == 2, "32- or 64-wide K stages");
-  static_assert((BM + BN) % (RPI * NW) == 0, "stage rows must split evenly over the waves");
+  static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "wave tiles are whole MFMA tiles");
   static_assert(SR * LDC * 2 <= SLAB, "staged output rows must fit in one stage buffer");
+  static_assert(WGN * BM * 4 <= SLAB, "the row sums of squares live in the second stage buffer");
+  static_assert((BM + BN) % RPI == 0, "a load instruction covers whole rows of one kind");
   static_assert(NS >= 2 && NS <= 6, "2 to 6 stages");
 };
 
 // One LDS array per stage: distinct objects let the compiler see that reading
 // one stage does not alias the loads in flight into the others.
 // ACT: the epilogue activation, fixed at compile time (-1: none; p.act must match).
+// MINB blocks must fit on a CU at once.  A block's waves are dealt over the
+// four SIMDs from the first, so each block can put ceil(NW / 4) waves on one
+// SIMD: the register budget is set for MINB times that many waves per SIMD
+// (six-wave blocks otherwise get a budget for three and run one block per CU).
 template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG, int ACT>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(MINB * ((WGM * WGN + 3) / 4))))
+void gemm_bf16_v2_kernel(GemmArgs p) {
   using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG>;
   constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
   __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
@@ -84,8 +107,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? C::SLAB : 16];
+  __shared__ __attribute__((aligned(1024))) char st_pad[C::PAD ? 1024 : 16];
   __shared__ int s_info[4];
-  __shared__ float s_sq[WGN][BM];
   char* const stages[6] = {st0, st1, st2, st3, st4, st5};
 
   const int n_tiles = (p.N + BN - 1) / BN;
@@ -104,7 +127,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
   // ---- this lane's load slots: instruction j = wave + NW i fills stage rows
   // RPI j .. RPI j + RPI - 1 (1 KB); lane l fills row RPI j + l / (4 SUB),
   // physical chunk l % (4 SUB), so each 4 SUB lanes fetch one row's 64 SUB
-  // contiguous bytes
+  // contiguous bytes.  Rows past BM + BN (the surplus instructions) read a
+  // clamped weight row into the dummy slot.
   const bf16_t* src[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -133,7 +157,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
         const int s = k / p.Kseg;
         off = (int64_t)s * N * p.Kseg + (k - s * p.Kseg);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + off), (lds_ptr_t)(base + row0 * C::RB), 16, 0, 0);
+      char* dst = (C::PAD && row0 >= BM + BN) ? st_pad : base + row0 * C::RB;  // uniform
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + off), (lds_ptr_t)dst, 16, 0, 0);
     }
   };
 
@@ -234,6 +259,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_bf16_v2_kernel(Gemm
   }
   bf16_t* Cs = (bf16_t*)st0;
   bf16_t* Cg = (bf16_t*)p.C;
+  float (*s_sq)[BM] = (float (*)[BM])st1;  // [WGN][BM]; the ring is idle now
   // pass i stages row tile i of every wave row (SR rows: staging row
   // 16 * wm + q holds tile row wm * WM + 16 i + q) and stores them
 #pragma unroll
@@ -315,10 +341,16 @@ bool gemm_v2_wide_k(const GemmArgs& a) { return a.K % 64 == 0 && (a.S <= 1 || a.
 // resident per CU each SIMD holds four or more waves, which hides the LDS and
 // barrier latency of one slab behind another wave's MFMAs (measured on
 // MI355X: 10-35 % faster than four waves with a 4-stage ring on the expert
-// shapes, bit-identical results).
+// shapes, bit-identical results).  The 144-row tiles use six waves in 3 x 2
+// (48 x 64 each, fewer LDS operand bytes per MFMA than 64 x 32): with a
+// 3-stage ring of 32-wide K stages two blocks share a CU; with 64-wide stages
+// one block runs alone with twice the K per barrier.  Every configuration
+// accumulates K in the same order, so all give the same bits.
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   if (tile == 512) return launch_v2<256, 256, 2, 4, 2, 2, 1>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2>(a, st);
+  if (tile == 144) return launch_v2<144, 128, 3, 2, 3, 1, 2>(a, st);
+  if (tile == 145) return launch_v2<144, 128, 3, 2, 3, 2, 1>(a, st);
   if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2>(a, st);
   return launch_v2<128, 128, 2, 4, 3, 1, 2>(a, st);
 }

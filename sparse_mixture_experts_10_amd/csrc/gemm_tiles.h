@@ -14,6 +14,7 @@ struct Tile {
 };
 
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin by id
+constexpr int kCus = 256; // MI355X compute units
 
 // Maps blockIdx.x to a (group, row tile, N tile).  The tile list is row-tile
 // major over the groups in order (so consecutive tiles share A rows and the

@@ -205,16 +205,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
     p.sq_part[(tl.row0 + tid) * (int64_t)n_tiles + tl.nt] = s_sq[0][tid] + s_sq[1][tid];
 }
 
-// Tile width the bf16 path uses for these arguments: large tiles only when
-// they still give every CU about two tiles.
 // Tile choice from host-side bounds (the row counts stay on the device):
 //   0    register-staged kernel (K not a multiple of 32)
 //   64   128 x 64 (narrow N)
-//   128  128 x 128, eight waves: small problems and small groups
+//   128  128 x 128, eight waves
+//   144  144 x 128, six waves, two blocks per CU
+//   145  144 x 128, six waves, 64-wide K stages, one block per CU
 //   256  256 x 128, eight waves: many tiles and groups of >= 512 rows
 //   512  256 x 256 with 64-wide K stages: groups of >= 1536 rows (the
 //        weight tiles are re-read from L2 the fewest times; measured on
 //        MI355X 3-9 % faster than 256 x 128 on the largest expert shapes)
+// Between 128 and 144 rows the one that puts the fewest rows on the busiest
+// CU wins, with every group assumed to hold its mean share plus 8 % (routing
+// imbalance).  A group of up to 1152 rows then takes eight 144-row tiles
+// instead of nine 128-row ones: on the 8-expert, 8192-row passes the tile
+// count drops to a whole number of waves over the CUs (measured on MI355X:
+// down pass 22 -> 17.7 us; the 64-wide-stage variant when one tile per CU
+// covers the pass).
 static int bf16_tile(const GemmArgs& a) {
   if (!gemm_v2_supported(a)) return 0;
   if (a.N <= 64) return 64;
@@ -222,7 +229,16 @@ static int bf16_tile(const GemmArgs& a) {
   const int64_t per_group = a.group_offset ? rows / a.G : rows;
   if (gemm_v2_wide_k(a) && a.N >= 512 && per_group >= 1536) return 512;
   const int64_t big = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 127) / 128);
-  return (big >= 1024 && per_group >= 512) ? 256 : 128;
+  if (big >= 1024 && per_group >= 512) return 256;
+  const int64_t nt = (a.N + 127) / 128;
+  const int64_t groups = a.group_offset ? a.G : 1;
+  const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
+  const int64_t t128 = groups * ((est + 127) / 128) * nt;
+  const int64_t t144 = groups * ((est + 143) / 144) * nt;
+  const int64_t cost128 = (t128 + kCus - 1) / kCus * 128;
+  const int64_t cost144 = (t144 + kCus - 1) / kCus * 144;
+  if (cost144 < cost128) return (t144 <= kCus && gemm_v2_wide_k(a)) ? 145 : 144;
+  return 128;
 }
 
 int gemm_bf16_n_tiles(const GemmArgs& a) {

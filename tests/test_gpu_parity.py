@@ -290,6 +290,54 @@ def test_grouped_gemm_repeatable_full_size(act, G, lo, hi, d, F):
     close_out(np.stack(got), np.stack(want), "bf16", "grouped gemm rows")
 
 
+def test_grouped_gemm_144_row_tiles():
+    """Eight ragged groups averaging 1024 rows at d 512, F 1024 (the default
+    workload's expert passes) take the 144-row tiles: six waves, two blocks a
+    CU on the up pass, 64-wide K stages on the down pass.  Groups of 40 and
+    1851 rows cover a partial tile and a group past eight tiles.  Every row of
+    both passes against a float32 product, the row sums of squares against
+    the float32 activations, and three runs agree bit for bit."""
+    counts = [1012, 970, 1047, 1160, 40, 1068, 1041, 1851]
+    G, d, F = len(counts), 512, 1024
+    off = torch.zeros(G + 1, dtype=torch.int32)
+    off[1:] = torch.cumsum(torch.tensor(counts), 0)
+    rows = int(off[-1])
+    say(f"[gpu] grouped gemm 144-row tiles G={G} rows={rows} d={d} F={F}")
+    g = torch.Generator(device="cuda").manual_seed(8)
+    a = torch.randn(rows, d, device="cuda", generator=g).to(torch.bfloat16)
+    W1 = (torch.randn(G, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(G, F, device="cuda", generator=g)).to(torch.bfloat16)
+    W2 = (torch.randn(G, d, F, device="cuda", generator=g) / F ** 0.5).to(torch.bfloat16)
+    b2 = (0.1 * torch.randn(G, d, device="cuda", generator=g)).to(torch.bfloat16)
+    goff = off.cuda()
+    ws = torch.empty(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dtype=torch.uint8, device="cuda")
+    runs = []
+    for _ in range(3):
+        hid = torch.zeros(rows, F, dtype=torch.bfloat16, device="cuda")
+        sq = torch.zeros(rows, dtype=torch.float32, device="cuda")
+        out = torch.zeros(rows, d, dtype=torch.bfloat16, device="cuda")
+        api.moe_expert_up(a, goff, rows, W1, b1, "gelu", hid, sq, ws)
+        api.moe_expert_down(hid, goff, rows, W2, b2, out)
+        runs.append((hid, sq, out))
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for x, y in zip(r, runs[0]):
+            assert torch.equal(x.view(torch.int32 if x.dtype == torch.float32 else torch.int16),
+                               y.view(torch.int32 if y.dtype == torch.float32 else torch.int16))
+    hid, sq, out = runs[0]
+    want_h, want_sq, want_o = [], [], []
+    for gi in range(G):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        z = a[r0:r1].float() @ W1[gi].float().t().contiguous() + b1[gi].float()
+        h = 0.5 * z * (1.0 + torch.erf(z / 2.0 ** 0.5))
+        want_h.append(h)
+        want_sq.append((h * h).sum(1))
+        want_o.append(hid[r0:r1].float() @ W2[gi].float().t().contiguous() + b2[gi].float())
+    close_out(f64(hid), torch.cat(want_h).double().cpu().numpy(), "bf16", "up pass, 144-row tiles")
+    np.testing.assert_allclose(f64(sq), torch.cat(want_sq).double().cpu().numpy(), rtol=1e-4)
+    close_out(f64(out), torch.cat(want_o).double().cpu().numpy(), "bf16", "down pass, 144-row tiles")
+
+
 @pytest.mark.parametrize("act", ["relu", "gelu", "swish"])
 def test_activation_accuracy(act):
     """The epilogue activations against their float64 definitions: an fp32 FFN
