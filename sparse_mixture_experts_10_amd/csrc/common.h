@@ -45,20 +45,24 @@ __device__ __forceinline__ vec16 pack_bf16x8(const float* f) {
 
 enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWISH = 2 };
 
-// GELU(z) = z Phi(z) = 0.5 z (1 + erf(z / sqrt 2)).  erfc(x) for x >= 0 by
-// Abramowitz & Stegun 7.1.26 (t = 1 / (1 + p x), erfc = t (a1 + t (a2 + ...)) e^{-x^2},
-// |error| <= 1.5e-7), with the hardware reciprocal and exp2; then
-// 1 + erf(z / sqrt 2) = 2 - erfc(|z| / sqrt 2) for z >= 0 and erfc(|z| / sqrt 2)
-// for z < 0.  About 15 instructions instead of the library erff's 45.
+// GELU(z) = z Phi(z) = 0.5 z (1 + erf(z / sqrt 2)).  Since
+// erf(z / sqrt 2) = sign(z) (1 - erfc(|z| / sqrt 2)), this is
+//   GELU(z) = max(z, 0) - 0.5 |z| erfc(|z| / sqrt 2).
+// erfc(x) for x >= 0 by Abramowitz & Stegun 7.1.26 (t = 1 / (1 + p x),
+// erfc = t (a1 + t (a2 + ...)) e^{-x^2}, |error| <= 1.5e-7), with the hardware
+// reciprocal and exp2 and x = |z| / sqrt 2 folded into the constants
+// (p x = (p / sqrt 2) |z|, x^2 log2(e) = z^2 log2(e) / 2): 12 VALU
+// instructions and two transcendentals.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188826636f, az, 1.0f));  // p / sqrt 2
   float p = fmaf(1.061405429f, t, -1.453152027f);
   p = fmaf(p, t, 1.421413741f);
   p = fmaf(p, t, -0.284496736f);
   p = fmaf(p, t, 0.254829592f);
-  const float q = p * t * __builtin_amdgcn_exp2f(-1.44269504088896341f * x * x);
-  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);  // e^{-z^2 / 2}
+  const float q = p * t * e;                                               // erfc(|z| / sqrt 2)
+  return fmaf(-0.5f * az, q, fmaxf(z, 0.0f));
 }
 
 // Swish / SiLU z sigmoid(z) = z / (1 + e^{-z}), with the hardware exp2 and

@@ -21,8 +21,10 @@
 // (one block per chunk) rebuilds from those counts the chunk's per-expert
 // arrival bases and the packed offsets (every block redundantly: no grid-wide
 // step), ranks each choice inside its chunk with a per-expert 64-bit token
-// mask, and copies the token rows when the packed copy is wanted.  Block 0
-// also writes the counts and offsets, and the statistics when asked.
+// mask, and copies the token rows when the packed copy is wanted.  One more
+// block writes the counts and offsets, and the statistics when asked.  Each
+// kernel issues its independent loads (the choices, the statistics inputs)
+// before waiting on any of them.
 
 #include "common.h"
 #include "internal.h"
@@ -31,6 +33,7 @@
 namespace moe {
 
 constexpr int kGroupChunks = kStatsTokens / kDispatchChunk;  // 4
+constexpr int kChoicePrefetch = 8;  // top-k choices a thread holds in registers
 
 // One block of 256 threads per group of 256 tokens.  Wave w counts chunk
 // 4 b + w.  hist[c][e], group[b][e]: counts; part[b][E + 1]: statistics
@@ -43,12 +46,26 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
   __shared__ double s_red[256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < kGroupChunks * kMaxExperts; i += 256) (&cnt[0][0])[i] = 0;
-  __syncthreads();
   const int64_t c = (int64_t)blockIdx.x * kGroupChunks + wave;
   const int64_t t = c * kDispatchChunk + lane;
-  if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt[wave][idx[t * k + j]], 1);
+  // this token's first kChoicePrefetch choices, in flight while the
+  // statistics partials load
+  int ch[kChoicePrefetch];
+#pragma unroll
+  for (int j = 0; j < kChoicePrefetch; ++j) ch[j] = (t < T && j < k) ? idx[t * k + j] : 0;
+  for (int i = tid; i < kGroupChunks * kMaxExperts; i += 256) (&cnt[0][0])[i] = 0;
+  if (logits != nullptr) {
+    const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
+    const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
+    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
+  }
+  __syncthreads();
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < kChoicePrefetch; ++j)
+      if (j < k) atomicAdd(&cnt[wave][ch[j]], 1);
+    for (int j = kChoicePrefetch; j < k; ++j) atomicAdd(&cnt[wave][idx[t * k + j]], 1);
+  }
   __syncthreads();
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   for (int e = tid; e < E; e += 256) {
@@ -60,11 +77,6 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
     }
     group[(int64_t)blockIdx.x * E + e] = sum;
   }
-  if (logits != nullptr) {
-    const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
-    const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
-    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
-  }
 }
 
 __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __restrict__ count,
@@ -75,7 +87,9 @@ __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __r
   }
 }
 
-// One block per chunk of 64 tokens; wave 0 ranks, all four waves copy rows.
+// One block per chunk of 64 tokens (wave 0 ranks, all four waves copy rows),
+// plus one bookkeeping block (blockIdx.x == nchunks) that writes the counts and
+// offsets and, in the fused routing pass, the statistics.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int ngroups,
@@ -92,12 +106,21 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   __shared__ int s_wsum[4];
   __shared__ int rows_s[kDispatchChunk * kMaxTopK];
   __shared__ double s_red[256];
+  __shared__ double s_z[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t c = blockIdx.x;
+  const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
+  const bool books = c == nchunks;  // uniform: the bookkeeping block
   const int64_t t = c * kDispatchChunk + lane;
-  const int64_t grp = c / kGroupChunks;
+  const int64_t grp = books ? ngroups : c / kGroupChunks;
+
+  // this token's first kChoicePrefetch choices (wave 0), in flight while the
+  // arrival bases load
+  int ch[kChoicePrefetch];
+#pragma unroll
+  for (int j = 0; j < kChoicePrefetch; ++j) ch[j] = (!books && wave == 0 && t < T && j < k) ? idx[t * k + j] : 0;
 
   // arrival base of this chunk and totals per expert.  Thread (q, e) sums
   // groups q, q + Q, ... (Q = 256 / E thread rows); integer sums, so the
@@ -120,7 +143,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
         pre += b < grp ? v : 0;
         tot += v;
       }
-      if (q == 0)
+      if (q == 0 && !books)
         for (int64_t cc = grp * kGroupChunks; cc < c; ++cc) pre += hist[cc * E + e];
     }
     s_scan[tid] = pre;
@@ -159,21 +182,30 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     if (tid == E - 1) s_off[E] = v;
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (books) {
     for (int e = tid; e < E; e += 256) count[e] = s_cnt[e];
     for (int e = tid; e <= E; e += 256) offset[e] = s_off[e];
-    if (f != nullptr) stats_finish(part, ngroups, s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red);
+    if (f != nullptr) stats_finish(part, ngroups, s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
+    return;
   }
 
-  if (wave == 0 && t < T)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[idx[t * k + j]], 1ull << lane);
+  if (wave == 0 && t < T) {
+#pragma unroll
+    for (int j = 0; j < kChoicePrefetch; ++j)
+      if (j < k) atomicOr(&mask[ch[j]], 1ull << lane);
+    for (int j = kChoicePrefetch; j < k; ++j) atomicOr(&mask[idx[t * k + j]], 1ull << lane);
+  }
   __syncthreads();
   if (wave == 0) {
     const uint64_t below = lanemask_lt();
     for (int j = 0; j < k; ++j) {
       int r = -1;
       if (t < T) {
-        const int e = idx[t * k + j];
+        int e = 0;
+#pragma unroll
+        for (int jj = 0; jj < kChoicePrefetch; ++jj)
+          if (jj == j) e = ch[jj];
+        if (j >= kChoicePrefetch) e = idx[t * k + j];
         const int s = s_base[e] + __popcll(mask[e] & below);
         slot[t * k + j] = s;
         if (cap < 0 || s < cap) {
@@ -219,7 +251,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
                      ws.hist, ws.group, stats ? stats->logits : nullptr, stats ? stats->lse : nullptr,
                      ws.part);
   const int64_t vpr = (int64_t)d * elem_bytes / 16;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, idx, T, k, E,
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)(nchunks + 1)), dim3(256), 0, st, idx, T, k, E,
                      capacity, ws.hist, ws.group, (int)ngroups, count, offset, slot, row, row_token,
                      (const vec16*)x, vpr, (vec16*)x_disp, ws.part, stats ? stats->alpha : 0.f,
                      stats ? stats->beta : 0.f, stats ? stats->f : nullptr, stats ? stats->P : nullptr,

@@ -56,9 +56,10 @@ __global__ __launch_bounds__(256) void stats_final_kernel(
     const float* __restrict__ credit_row, float* __restrict__ mean_credit,
     const float* __restrict__ loss_row, float* __restrict__ expert_loss) {
   __shared__ double s_red[256];
+  __shared__ double s_z[256];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
-    stats_finish(part, nparts, count, T, E, k, alpha, beta, f, Pm, losses, s_red);
+    stats_finish(part, nparts, count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
     return;
   }
   const int e = blockIdx.x - 1;

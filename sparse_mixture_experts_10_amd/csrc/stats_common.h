@@ -64,30 +64,62 @@ __device__ __forceinline__ void stats_block_partials(const float* __restrict__ l
 }
 
 // One 256-thread block: f, P and the losses from the block partials
-// part[nparts][E + 1] and the pre-capacity counts.  s_red: 256 doubles.
+// part[nparts][E + 1] and the pre-capacity counts.  Fixed order, all partial
+// loads in flight together: expert column e is summed by Q = 256 / E threads,
+// thread q taking partials q, q + Q, ... in order, then the Q sums in q order;
+// the lse^2 column by all 256 threads (partials tid, tid + 256, ...) and a
+// pairwise tree.  s_red: 256 doubles; s_z: 256 doubles.
 __device__ __forceinline__ void stats_finish(const double* __restrict__ part, int nparts,
                                              const int32_t* count, int64_t T, int E, int k,
                                              float alpha, float beta, float* __restrict__ f,
                                              float* __restrict__ Pm, float* __restrict__ losses,
-                                             double* s_red) {
+                                             double* s_red, double* s_z) {
   const int tid = threadIdx.x;
+  const int C = E + 1;
+  const int Q = 256 / E;
+  {
+    const int e = tid % E, q = tid / E;
+    double s = 0.0;
+    if (q < Q) {
+      int b = q;
+      for (; b + 3 * Q < nparts; b += 4 * Q) {
+        const double v0 = part[(int64_t)b * C + e], v1 = part[(int64_t)(b + Q) * C + e];
+        const double v2 = part[(int64_t)(b + 2 * Q) * C + e], v3 = part[(int64_t)(b + 3 * Q) * C + e];
+        s += v0;
+        s += v1;
+        s += v2;
+        s += v3;
+      }
+      for (; b < nparts; b += Q) s += part[(int64_t)b * C + e];
+    }
+    double z = 0.0;
+    for (int b = tid; b < nparts; b += 256) z += part[(int64_t)b * C + E];
+    s_red[tid] = s;
+    s_z[tid] = z;
+  }
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_z[tid] += s_z[tid + w];
+    __syncthreads();
+  }
+  double fp_e = 0.0;
   if (tid < E) {
     double s = 0.0;
-    for (int b = 0; b < nparts; ++b) s += part[(int64_t)b * (E + 1) + tid];
+    for (int q = 0; q < Q; ++q) s += s_red[q * E + tid];
     const double pe = s / (double)T;
     const double fe = (double)count[tid] / ((double)k * (double)T);
     Pm[tid] = (float)pe;
     f[tid] = (float)fe;
-    s_red[tid] = fe * pe;
+    fp_e = fe * pe;
   }
+  __syncthreads();
+  if (tid < E) s_red[tid] = fp_e;
   __syncthreads();
   if (tid == 0) {
     double fp = 0.0;
     for (int ee = 0; ee < E; ++ee) fp += s_red[ee];
-    double z = 0.0;
-    for (int b = 0; b < nparts; ++b) z += part[(int64_t)b * (E + 1) + E];
     const double la = (double)alpha * (double)E * fp;
-    const double lz = (double)beta * z / (double)T;
+    const double lz = (double)beta * s_z[0] / (double)T;
     losses[0] = (float)la;
     losses[1] = (float)lz;
     losses[2] = (float)(la + lz);
