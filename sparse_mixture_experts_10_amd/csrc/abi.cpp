@@ -54,7 +54,32 @@ DispatchWs dispatch_ws_layout(void* ws, int64_t T, int32_t E) {
   return w;
 }
 
+// The fused routing pass counts inside the router (no counting kernel) when
+// the K-split router runs and the per-16-token counts stay few enough for
+// every scatter block to sum them.
+static bool route_counts_in_router(int64_t T, int32_t d, int32_t E, bool xbf16) {
+  const int64_t units = (T + kStatsSub - 1) / kStatsSub;
+  return router_uses_ksplit(xbf16, d, E) && units * (int64_t)E <= 8192;
+}
+
+// counting-router layout: per-16-token counts [units][E], then the statistics
+// sub-partials [units][E + 1]
+static DispatchWs route_units_layout(void* ws, int64_t T, int32_t E) {
+  const int64_t units = (T + kStatsSub - 1) / kStatsSub;
+  DispatchWs w;
+  w.hist = nullptr;
+  w.group = (int32_t*)ws;
+  w.part = (double*)((char*)ws + align_up((size_t)units * (size_t)E * sizeof(int32_t)));
+  w.units16 = true;
+  return w;
+}
+
 size_t route_ws(int64_t T, int32_t d, int32_t E, bool xbf16) {
+  if (route_counts_in_router(T, d, E, xbf16)) {
+    const int64_t units = (T + kStatsSub - 1) / kStatsSub;
+    return align_up((size_t)units * (size_t)E * sizeof(int32_t)) +
+           align_up((size_t)units * (size_t)(E + 1) * sizeof(double));
+  }
   const size_t r = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
   return r + dispatch_ws(T, E, true);
 }
@@ -235,13 +260,23 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
   const size_t need = route_ws(T, d, E, xbf16);
   if (need > 0 && (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0))
     return MOE_ERR_WORKSPACE;
+  RouteStats rs{logits, lse, alpha, beta, f, P, losses};
+  if (T > 0 && route_counts_in_router(T, d, E, xbf16)) {
+    // two kernels: the counting router, then the scatter
+    const DispatchWs w = route_units_layout(ws, T, E);
+    const hipError_t e = launch_router_counting(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
+                                                topk_idx, topk_gate, noise, (double)noise_std, w.group,
+                                                w.part, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
+                                      expert_offset, slot, row, row_token, nullptr, w, &rs, stream));
+  }
   const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
   if (T > 0) {
     const hipError_t e = launch_router(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse, topk_idx,
                                        topk_gate, noise, (double)noise_std, ws, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  RouteStats rs{logits, lse, alpha, beta, f, P, losses};
   return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
                                     expert_offset, slot, row, row_token, nullptr,
                                     dispatch_ws_layout((char*)ws + rws, T, E), T > 0 ? &rs : nullptr,

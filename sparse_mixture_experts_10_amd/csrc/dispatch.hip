@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __r
 // offsets and, in the fused routing pass, the statistics.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap,
-    const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int ngroups,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int nunits, int unit_tokens,
     int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot,
     int32_t* __restrict__ row, int32_t* __restrict__ row_token, const vec16* __restrict__ x,
     int64_t vecs_per_row, vec16* __restrict__ x_disp, const double* __restrict__ part, float alpha,
@@ -101,8 +101,6 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   __shared__ int s_base[kMaxExperts];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_scan[256];
-  __shared__ int s_red_i[256];
   __shared__ int s_wsum[4];
   __shared__ int rows_s[kDispatchChunk * kMaxTopK];
   __shared__ double s_red[256];
@@ -114,52 +112,73 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   const bool books = c == nchunks;  // uniform: the bookkeeping block
   const int64_t t = c * kDispatchChunk + lane;
-  const int64_t grp = books ? ngroups : c / kGroupChunks;
+  const int64_t grp = books ? nunits : c * kDispatchChunk / unit_tokens;  // units before the chunk
 
+  for (int e = tid; e < E; e += 256) {
+    s_base[e] = 0;
+    s_cnt[e] = 0;
+  }
   // this token's first kChoicePrefetch choices (wave 0), in flight while the
   // arrival bases load
   int ch[kChoicePrefetch];
 #pragma unroll
   for (int j = 0; j < kChoicePrefetch; ++j) ch[j] = (!books && wave == 0 && t < T && j < k) ? idx[t * k + j] : 0;
 
-  // arrival base of this chunk and totals per expert.  Thread (q, e) sums
-  // groups q, q + Q, ... (Q = 256 / E thread rows); integer sums, so the
+  // arrival base of this chunk and totals per expert from the per-unit counts
+  // (units of 256 tokens, plus the per-chunk counts inside the chunk's unit;
+  // or units of 16 tokens).  Thread (q, e) sums units q, q + Q, ...
+  // (Q = 256 / E thread rows), eight loads in flight; integer sums, so the
   // split does not change the result.
   {
     const int Q = 256 / E;
     const int e = tid % E, q = tid / E;
     int pre = 0, tot = 0;
+    // the first eight units' counts go out before the bookkeeping block's
+    // statistics loads, so the two wait together
+    int v0[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v0[u] = (q < Q && q + u * Q < nunits) ? group[(int64_t)(q + u * Q) * E + e] : 0;
+    if (books && f != nullptr) {
+      const bool sub = unit_tokens == kStatsSub;
+      const int ngroups = sub ? (nunits + kStatsSubs - 1) / kStatsSubs : nunits;
+      stats_finish_sums(part, ngroups, E, s_red, s_z, sub ? nunits : 0);
+    }
     if (q < Q) {
-      int b = q;
-      for (; b + 3 * Q < ngroups; b += 4 * Q) {
-        const int v0 = group[(int64_t)b * E + e], v1 = group[(int64_t)(b + Q) * E + e];
-        const int v2 = group[(int64_t)(b + 2 * Q) * E + e], v3 = group[(int64_t)(b + 3 * Q) * E + e];
-        pre += (b < grp ? v0 : 0) + (b + Q < grp ? v1 : 0) + (b + 2 * Q < grp ? v2 : 0) +
-               (b + 3 * Q < grp ? v3 : 0);
-        tot += v0 + v1 + v2 + v3;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pre += (q + u * Q < grp) ? v0[u] : 0;
+        tot += v0[u];
       }
-      for (; b < ngroups; b += Q) {
+      int b = q + 8 * Q;
+      for (; b + 7 * Q < nunits; b += 8 * Q) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = group[(int64_t)(b + u * Q) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          pre += (b + u * Q < grp) ? v[u] : 0;
+          tot += v[u];
+        }
+      }
+      for (; b < nunits; b += Q) {
         const int v = group[(int64_t)b * E + e];
         pre += b < grp ? v : 0;
         tot += v;
       }
-      if (q == 0 && !books)
+      if (q == 0 && !books && unit_tokens > kDispatchChunk)
         for (int64_t cc = grp * kGroupChunks; cc < c; ++cc) pre += hist[cc * E + e];
     }
-    s_scan[tid] = pre;
-    s_red_i[tid] = tot;
+    __syncthreads();  // the zeroed sums
+    if (q < Q) {
+      // integer sums: LDS atomics combine the Q thread rows in any order
+      atomicAdd(&s_base[e], pre);
+      atomicAdd(&s_cnt[e], tot);
+    }
   }
   __syncthreads();
   int kept = 0;
   if (tid < E) {
-    const int Q = 256 / E;
-    int pre = 0, tot = 0;
-    for (int q = 0; q < Q; ++q) {
-      pre += s_scan[q * E + tid];
-      tot += s_red_i[q * E + tid];
-    }
-    s_base[tid] = pre;
-    s_cnt[tid] = tot;
+    const int tot = s_cnt[tid];
     kept = (cap < 0 || tot < cap) ? tot : (int)cap;
     mask[tid] = 0ull;
   }
@@ -185,7 +204,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   if (books) {
     for (int e = tid; e < E; e += 256) count[e] = s_cnt[e];
     for (int e = tid; e <= E; e += 256) offset[e] = s_off[e];
-    if (f != nullptr) stats_finish(part, ngroups, s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
+    // statistics: the sums were taken above (group values stored for units of
+    // 256, summed from the 16-token sub-partials otherwise: the same order)
+    if (f != nullptr) stats_finish_write(s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
     return;
   }
 
@@ -247,12 +268,20 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
     hipLaunchKernelGGL(dispatch_empty_kernel, dim3(1), dim3(256), 0, st, E, count, offset);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3((unsigned)ngroups), dim3(256), 0, st, idx, T, k, E,
-                     ws.hist, ws.group, stats ? stats->logits : nullptr, stats ? stats->lse : nullptr,
-                     ws.part);
+  int unit = kStatsTokens;
+  int64_t nunits = ngroups;
+  if (ws.units16) {
+    // the counting router wrote the per-16-token counts and sub-partials
+    unit = kStatsSub;
+    nunits = (T + kStatsSub - 1) / kStatsSub;
+  } else {
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3((unsigned)ngroups), dim3(256), 0, st, idx, T, k, E,
+                       ws.hist, ws.group, stats ? stats->logits : nullptr, stats ? stats->lse : nullptr,
+                       ws.part);
+  }
   const int64_t vpr = (int64_t)d * elem_bytes / 16;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)(nchunks + 1)), dim3(256), 0, st, idx, T, k, E,
-                     capacity, ws.hist, ws.group, (int)ngroups, count, offset, slot, row, row_token,
+                     capacity, ws.hist, ws.group, (int)nunits, unit, count, offset, slot, row, row_token,
                      (const vec16*)x, vpr, (vec16*)x_disp, ws.part, stats ? stats->alpha : 0.f,
                      stats ? stats->beta : 0.f, stats ? stats->f : nullptr, stats ? stats->P : nullptr,
                      stats ? stats->losses : nullptr);

@@ -14,6 +14,7 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kDispatchChunk = 64;    // tokens per dispatch chunk (one wavefront)
 constexpr int kStatsTokens = 256;     // tokens per statistics partial block
+constexpr int kStatsSub = 16;         // tokens per statistics sub-partial (and router block)
 constexpr int kGemmBN = 128;          // N tile of the bf16 grouped GEMM
 constexpr int kGemmBM = 128;          // M tile of the bf16 grouped GEMM
 constexpr int kGemmF32BN = 64;        // N tile of the fp32 grouped GEMM
@@ -33,14 +34,26 @@ hipError_t launch_mlp_router(const void* x, bool xbf16, int64_t T, int d, const 
 size_t mlp_router_ws_bytes(int64_t T, int H);
 bool router_uses_mfma(bool xbf16, int d, int E);
 size_t router_mfma_ws_bytes(int64_t T, int d, int E);
+bool router_uses_ksplit(bool xbf16, int d, int E);
+// The K-split router that also counts: per block of 16 tokens it writes the
+// choices per expert, hist16 [ceil(T / 16)][E], and the statistics
+// sub-partials, p16 [ceil(T / 16)][E + 1] (only when router_uses_ksplit()).
+hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
+                                  const float* bg, const float* bsel, int E, int k, float* logits,
+                                  float* lse, int32_t* idx, float* gate, const float* noise,
+                                  double sigma, int32_t* hist16, double* p16, hipStream_t st);
 
 // Dispatch scratch: per-chunk counts [nchunks][E], per-group counts
 // [ngroups][E] (a group is kStatsTokens tokens), and, for the fused routing
-// pass, statistics partials [ngroups][E + 1].
+// pass, statistics partials [ngroups][E + 1].  With units16 the counting
+// router has already written per-16-token counts into group ([ceil(T/16)][E])
+// and the statistics sub-partials into part ([ceil(T/16)][E + 1]); hist is
+// unused and no counting kernel runs.
 struct DispatchWs {
   int32_t* hist;
   int32_t* group;
   double* part;
+  bool units16 = false;
 };
 // Routing statistics taken in the same pass as the dispatch (nullptr: none).
 struct RouteStats {

@@ -122,6 +122,15 @@ __device__ __forceinline__ void group_argmax(double& s, int& e, float& x) {
   if constexpr (NXE > 32) argmax_step<32>(s, e, x);
 }
 
+// Optional per-token record of the epilogue: the softmax mass per expert and
+// the lse (this token's LDS rows), and a count per selected expert (LDS
+// integer atomics into the block's histogram: order-free).
+struct RouterTap {
+  float* p;     // [E]
+  float* lse;   // [1]
+  int* hist;    // [E], shared by the block
+};
+
 // Per-token epilogue.  The NXE lanes of a token hold its fp64 dot products
 // (router bias not yet added): lane eg holds experts e = eg + NXE j, j < TE.
 // With noise != nullptr the logits are h + sigma * noise[t, e] (noisy top-k,
@@ -141,7 +150,7 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
                                                int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_gate,
                                                const float* __restrict__ noise, double sigma,
-                                               double flag_rel = 0.0) {
+                                               double flag_rel = 0.0, RouterTap* tap = nullptr) {
   const double NEG = -__builtin_huge_val();
   double h[TE], s[TE];
   double m = NEG;
@@ -173,6 +182,17 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
       if (e < E) logits[t * E + e] = (float)h[j];
     }
     if (eg == 0) lse_out[t] = (float)(m + (double)logf(se));
+  }
+  if (tap != nullptr) {
+    // the softmax mass as the statistics take it: expf(logit - lse) on the
+    // stored fp32 values
+    const float lse_f = (float)(m + (double)logf(se));
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = eg + NXE * j;
+      if (e < E) tap->p[e] = expf((float)h[j] - lse_f);
+    }
+    if (eg == 0) *tap->lse = lse_f;
   }
   // k argmax rounds in selection order (one more for the near-tie flag); the
   // lane owning a selected expert records its round, and once the sum of the
@@ -216,6 +236,7 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
       if ((taken >> j) & 1u) {
         topk_idx[t * k + rank[j]] = eg + NXE * j;
         topk_gate[t * k + rank[j]] = ex[j] / gsum;
+        if (tap != nullptr) atomicAdd(&tap->hist[eg + NXE * j], 1);
       }
     }
   }
@@ -396,6 +417,7 @@ __device__ __forceinline__ void rs_halve(const double (&v)[N], double (&w)[N / 2
 
 constexpr int KS_LPT = 16;    // lanes per token
 constexpr int KS_TPB = 16;    // tokens per block (256 threads)
+static_assert(KS_TPB == kStatsSub, "a counting router block is one statistics sub-block");
 constexpr int KS_XV = 16;     // x vectors per lane: d <= 16 * 16 * 8 (bf16) or 16 * 16 * 4 (fp32)
 constexpr int KS_FB = 4;      // W_g float4 loads a thread has in flight during the LDS fill
 
@@ -424,8 +446,14 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma,
+    int32_t* __restrict__ hist16, double* __restrict__ p16) {
   extern __shared__ float4 wsm[];  // W_g, fp32, in the chunked layout above
+  // fused routing pass (hist16 != nullptr): this block's 16 tokens as one
+  // counting unit and one statistics sub-partial
+  __shared__ float tap_p[KS_TPB][EP];
+  __shared__ float tap_lse[KS_TPB];
+  __shared__ int tap_hist[EP];
   constexpr int XW = XBF16 ? 8 : 4;   // elements per 16-byte x vector
   constexpr int CH = KS_LPT * XW;     // columns per chunk
   constexpr int CH4 = CH / 4;         // float4 per chunk
@@ -451,6 +479,8 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
                      : *(const vec16*)((const float*)xv + t * (int64_t)d + col);
     }
   }
+
+  if (hist16 != nullptr && tid < EP) tap_hist[tid] = 0;  // ordered before use by the fill's barrier
 
   // W_g -> LDS, EP rows (rows past E and columns past d are zero): KS_FB loads
   // in flight per thread, then their stores
@@ -539,23 +569,52 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     rs_halve<EP / 8, 1>(b2, r, lane);
   }
   // for EP = 8, lanes 8..15 duplicate lanes 0..7; their expert ids lane >= 8 >= E are void
+  const int tl = tid / KS_LPT;
+  RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
   token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                             noise, sigma);
+                             noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+  if (hist16 == nullptr) return;  // uniform
+  __syncthreads();
+  // per expert: choices among the block's tokens and the softmax mass summed
+  // in token order; thread E: the lse^2 sum (the statistics sub-partial)
+  const int64_t t0 = (int64_t)blockIdx.x * KS_TPB;
+  const int nt = (int)((T - t0) < KS_TPB ? (T - t0) : KS_TPB);
+  if (tid < E) {
+    float v[KS_TPB];
+#pragma unroll
+    for (int u = 0; u < KS_TPB; ++u) v[u] = tap_p[u][tid];
+    double m = 0.0;
+#pragma unroll
+    for (int u = 0; u < KS_TPB; ++u)
+      if (u < nt) m += (double)v[u];
+    hist16[blockIdx.x * (int64_t)E + tid] = tap_hist[tid];
+    p16[blockIdx.x * (int64_t)(E + 1) + tid] = m;
+  } else if (tid == E) {
+    float v[KS_TPB];
+#pragma unroll
+    for (int u = 0; u < KS_TPB; ++u) v[u] = tap_lse[u];
+    double z = 0.0;
+#pragma unroll
+    for (int u = 0; u < KS_TPB; ++u)
+      if (u < nt) z += (double)v[u] * (double)v[u];
+    p16[blockIdx.x * (int64_t)(E + 1) + E] = z;
+  }
 }
 
 template <int EP>
 static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                        const float* bg, const float* bsel, int E, int k,
                                        float* logits, float* lse, int32_t* idx, float* gate,
-                                       const float* noise, double sigma, hipStream_t st) {
+                                       const float* noise, double sigma, int32_t* hist16,
+                                       double* p16, hipStream_t st) {
   const dim3 grid((unsigned)((T + KS_TPB - 1) / KS_TPB));
   const size_t lds = ks_lds_bytes(E, d, xbf16);
   if (xbf16)
     hipLaunchKernelGGL((router_ksplit_kernel<EP, true>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate, noise, sigma);
+                       bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16);
   else
     hipLaunchKernelGGL((router_ksplit_kernel<EP, false>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate, noise, sigma);
+                       bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16);
   return hipGetLastError();
 }
 
@@ -761,6 +820,28 @@ static hipError_t launch_router_e_split(const void* x, int xt, int64_t T, int d,
 #undef MOE_ROUTER_EP
 }
 
+// K-split when W_g (EP padded rows) fits in 64 KB of LDS and E <= 64 (and the
+// MFMA path does not apply); the LDS bound also keeps the chunk count within
+// the kernel's x vectors
+bool router_uses_ksplit(bool xbf16, int d, int E) {
+  return !router_uses_mfma(xbf16, d, E) && ks_lds_bytes(E, d, xbf16) <= 65536 && E <= 64 &&
+         d <= KS_XV * ks_chunk_cols(xbf16);
+}
+
+hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
+                                  const float* bg, const float* bsel, int E, int k, float* logits,
+                                  float* lse, int32_t* idx, float* gate, const float* noise,
+                                  double sigma, int32_t* hist16, double* p16, hipStream_t st) {
+#define MOE_ROUTER_KSC(EPV) \
+  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, \
+                                   hist16, p16, st)
+  if (E <= 8) MOE_ROUTER_KSC(8);
+  if (E <= 16) MOE_ROUTER_KSC(16);
+  if (E <= 32) MOE_ROUTER_KSC(32);
+  MOE_ROUTER_KSC(64);
+#undef MOE_ROUTER_KSC
+}
+
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
                          float* lse, int32_t* idx, float* gate, const float* noise, double sigma,
@@ -773,11 +854,10 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
     MOE_ROUTER_MFMA(256);
 #undef MOE_ROUTER_MFMA
   }
-  // K-split when W_g (EP padded rows) fits in 64 KB of LDS and E <= 64; the LDS bound
-  // also keeps the chunk count within the kernel's x vectors
-  if (ks_lds_bytes(E, d, xbf16) <= 65536 && E <= 64 && d <= KS_XV * ks_chunk_cols(xbf16)) {
+  if (router_uses_ksplit(xbf16, d, E)) {
 #define MOE_ROUTER_KS(EPV) \
-  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
+  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, \
+                                   nullptr, nullptr, st)
     if (E <= 8) MOE_ROUTER_KS(8);
     if (E <= 16) MOE_ROUTER_KS(16);
     if (E <= 32) MOE_ROUTER_KS(32);

@@ -4,8 +4,11 @@
 // Page "Appendix C -- Acronyms & Symbols", Balancing:
 //   f_e   = count_e / (k T)            P_e = (1/T) sum_t softmax(h_t)_e
 //   L_aux = alpha E sum_e f_e P_e      L_z = beta (1/T) sum_t lse_t^2
-// All sums are fp64 in a fixed order: per block of kStatsTokens tokens first,
-// then over the blocks in block order.
+// All sums are fp64 in one fixed order, whichever kernel takes them:
+//   sub-partial  = sum over a block of kStatsSub tokens, in token order, from 0
+//   group value  = sum of the group's sub-partials (kStatsTokens tokens), in order
+//   total        = stats_finish's fixed order over the group values
+// The softmax mass of a token is expf(logit - lse) on the stored fp32 values.
 #pragma once
 
 #include "common.h"
@@ -13,67 +16,83 @@
 
 namespace moe {
 
-// One 256-thread block: softmax mass per expert and the lse^2 sum over tokens
-// [t0, t1) (t1 - t0 <= 256) into out[0..E-1] and out[E].  s_red: 256 doubles.
+constexpr int kStatsSubs = kStatsTokens / kStatsSub;  // sub-partials per group
+
+// One 256-thread block: the group value of tokens [t0, t1) (t1 - t0 <= 256):
+// softmax mass per expert into out[0..E-1], lse^2 into out[E].  Experts go in
+// rounds of 16: thread (i, el) sums sub-block i of expert e0 + el.
+// s_red: 256 doubles.
 __device__ __forceinline__ void stats_block_partials(const float* __restrict__ logits,
                                                      const float* __restrict__ lse, int64_t t0,
                                                      int64_t t1, int E, double* s_red,
                                                      double* __restrict__ out) {
   const int tid = threadIdx.x;
-  // thread (grp, e) sums the mass of tokens t0 + grp, t0 + grp + ngrp, ...
-  const int ngrp = 256 / E;
-  const int e = tid % E, grp = tid / E;
-  double m = 0.0;
-  if (grp < ngrp) {
-    // tokens in order; eight loads issued ahead of their eight ordered adds
-    int64_t t = t0 + grp;
-    for (; t + 7 * ngrp < t1; t += 8 * ngrp) {
-      float h[8], l[8];
+  const int i = tid / kStatsSub, el = tid % kStatsSub;   // sub-block, expert in the round
+  const int64_t s0 = t0 + (int64_t)i * kStatsSub;
+  const int n = (int)((t1 - s0) < kStatsSub ? (t1 - s0 > 0 ? t1 - s0 : 0) : kStatsSub);
+  float l[kStatsSub];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        h[u] = logits[(t + u * ngrp) * E + e];
-        l[u] = lse[t + u * ngrp];
-      }
+  for (int u = 0; u < kStatsSub; ++u) l[u] = u < n ? lse[s0 + u] : 0.f;
+  for (int e0 = 0; e0 < E; e0 += kStatsSub) {
+    const int e = e0 + el;
+    double m = 0.0;
+    if (e < E) {
+      float h[kStatsSub];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) m += (double)expf(h[u] - l[u]);
+      for (int u = 0; u < kStatsSub; ++u) h[u] = u < n ? logits[(s0 + u) * E + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kStatsSub; ++u)
+        if (u < n) m += (double)expf(h[u] - l[u]);
     }
-    for (; t < t1; t += ngrp) m += (double)expf(logits[t * E + e] - lse[t]);
-  }
-  s_red[tid] = m;
-  __syncthreads();
-  if (tid < E) {
-    double s = 0.0;
-    for (int q = 0; q < ngrp; ++q) s += s_red[q * E + tid];
-    out[tid] = s;
-  }
-  __syncthreads();
-  const int64_t t = t0 + tid;
-  double z = 0.0;
-  if (t < t1) {
-    const double l = (double)lse[t];
-    z = l * l;
-  }
-  s_red[tid] = z;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] += s_red[tid + w];
+    s_red[tid] = m;
+    __syncthreads();
+    if (tid < kStatsSub && e0 + tid < E) {
+      double g = 0.0;
+      for (int q = 0; q < kStatsSubs; ++q) g += s_red[q * kStatsSub + tid];
+      out[e0 + tid] = g;
+    }
     __syncthreads();
   }
-  if (tid == 0) out[E] = s_red[0];
+  // lse^2: lane el == 0 of each sub-block, then the sub-blocks in order
+  double z = 0.0;
+#pragma unroll
+  for (int u = 0; u < kStatsSub; ++u)
+    if (u < n) z += (double)l[u] * (double)l[u];
+  s_red[tid] = z;
+  __syncthreads();
+  if (tid == 0) {
+    double g = 0.0;
+    for (int q = 0; q < kStatsSubs; ++q) g += s_red[q * kStatsSub];
+    out[E] = g;
+  }
   __syncthreads();
 }
 
-// One 256-thread block: f, P and the losses from the block partials
-// part[nparts][E + 1] and the pre-capacity counts.  Fixed order, all partial
-// loads in flight together: expert column e is summed by Q = 256 / E threads,
-// thread q taking partials q, q + Q, ... in order, then the Q sums in q order;
-// the lse^2 column by all 256 threads (partials tid, tid + 256, ...) and a
-// pairwise tree.  s_red: 256 doubles; s_z: 256 doubles.
-__device__ __forceinline__ void stats_finish(const double* __restrict__ part, int nparts,
-                                             const int32_t* count, int64_t T, int E, int k,
-                                             float alpha, float beta, float* __restrict__ f,
-                                             float* __restrict__ Pm, float* __restrict__ losses,
-                                             double* s_red, double* s_z) {
+// Value of group b, column col: stored directly (nsub == 0: part is
+// [ngroups][C]) or summed from its sub-partials (part is [nsub][C], the
+// group's kStatsSubs rows in order).
+__device__ __forceinline__ double stats_group_value(const double* __restrict__ part, int64_t b, int col,
+                                                    int C, int64_t nsub) {
+  if (nsub == 0) return part[b * C + col];
+  const int64_t r0 = b * kStatsSubs;
+  double v[kStatsSubs];
+#pragma unroll
+  for (int i = 0; i < kStatsSubs; ++i) v[i] = (r0 + i < nsub) ? part[(r0 + i) * C + col] : 0.0;
+  double g = 0.0;
+#pragma unroll
+  for (int i = 0; i < kStatsSubs; ++i) g += v[i];
+  return g;
+}
+
+// One 256-thread block, first half of the statistics finish: the sums over
+// the group values (nparts groups; see stats_group_value for nsub) in a
+// fixed order, all partial loads in flight together.  Expert column e is
+// summed by Q = 256 / E threads, thread q taking groups q, q + Q, ... in
+// order (left in s_red[q E + e]); the lse^2 column by all 256 threads
+// (groups tid, tid + 256, ...) and a pairwise tree (left in s_z[0]).
+// s_red, s_z: 256 doubles each.
+__device__ __forceinline__ void stats_finish_sums(const double* __restrict__ part, int nparts, int E,
+                                                  double* s_red, double* s_z, int64_t nsub = 0) {
   const int tid = threadIdx.x;
   const int C = E + 1;
   const int Q = 256 / E;
@@ -83,17 +102,19 @@ __device__ __forceinline__ void stats_finish(const double* __restrict__ part, in
     if (q < Q) {
       int b = q;
       for (; b + 3 * Q < nparts; b += 4 * Q) {
-        const double v0 = part[(int64_t)b * C + e], v1 = part[(int64_t)(b + Q) * C + e];
-        const double v2 = part[(int64_t)(b + 2 * Q) * C + e], v3 = part[(int64_t)(b + 3 * Q) * C + e];
+        const double v0 = stats_group_value(part, b, e, C, nsub);
+        const double v1 = stats_group_value(part, b + Q, e, C, nsub);
+        const double v2 = stats_group_value(part, b + 2 * Q, e, C, nsub);
+        const double v3 = stats_group_value(part, b + 3 * Q, e, C, nsub);
         s += v0;
         s += v1;
         s += v2;
         s += v3;
       }
-      for (; b < nparts; b += Q) s += part[(int64_t)b * C + e];
+      for (; b < nparts; b += Q) s += stats_group_value(part, b, e, C, nsub);
     }
     double z = 0.0;
-    for (int b = tid; b < nparts; b += 256) z += part[(int64_t)b * C + E];
+    for (int b = tid; b < nparts; b += 256) z += stats_group_value(part, b, E, C, nsub);
     s_red[tid] = s;
     s_z[tid] = z;
   }
@@ -102,6 +123,15 @@ __device__ __forceinline__ void stats_finish(const double* __restrict__ part, in
     if (tid < w) s_z[tid] += s_z[tid + w];
     __syncthreads();
   }
+}
+
+// Second half: f, P and the losses from those sums and the pre-capacity counts.
+__device__ __forceinline__ void stats_finish_write(const int32_t* count, int64_t T, int E, int k,
+                                                   float alpha, float beta, float* __restrict__ f,
+                                                   float* __restrict__ Pm, float* __restrict__ losses,
+                                                   double* s_red, double* s_z) {
+  const int tid = threadIdx.x;
+  const int Q = 256 / E;
   double fp_e = 0.0;
   if (tid < E) {
     double s = 0.0;
@@ -124,6 +154,15 @@ __device__ __forceinline__ void stats_finish(const double* __restrict__ part, in
     losses[1] = (float)lz;
     losses[2] = (float)(la + lz);
   }
+}
+
+__device__ __forceinline__ void stats_finish(const double* __restrict__ part, int nparts,
+                                             const int32_t* count, int64_t T, int E, int k,
+                                             float alpha, float beta, float* __restrict__ f,
+                                             float* __restrict__ Pm, float* __restrict__ losses,
+                                             double* s_red, double* s_z, int64_t nsub = 0) {
+  stats_finish_sums(part, nparts, E, s_red, s_z, nsub);
+  stats_finish_write(count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
 }
 
 }  // namespace moe
