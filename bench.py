@@ -266,7 +266,7 @@ def main():
         "config": {"workload": w.name, "T": T, "d": d, "E": E, "k": k, "F": F, "act": w.act,
                    "capacity_factor": None if w.capacity_factor is None else str(w.capacity_factor),
                    "n_shared": w.n_shared, "kept_rows": rows},
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (expert up + down, 2 launches/step)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_v2_kernel (expert up + down, 2 launches/step)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": counter_traffic(w.name),
                      "algorithmic_bytes": gemm_bytes},
