@@ -215,9 +215,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 //   512  256 x 256 with 64-wide K stages: groups of >= 1536 rows (the
 //        weight tiles are re-read from L2 the fewest times; measured on
 //        MI355X 3-9 % faster than 256 x 128 on the largest expert shapes)
-// Between 128 and 144 rows the one that puts the fewest rows on the busiest
-// CU wins, with every group assumed to hold its mean share plus 8 % (routing
-// imbalance).  A group of up to 1152 rows then takes eight 144-row tiles
+// Between 128 and 144 rows, for passes of at most four waves of 128-row tiles,
+// the one that puts the fewest rows on the busiest CU wins, with every group
+// assumed to hold its mean share plus 8 % (routing imbalance).  A group of up to 1152 rows then takes eight 144-row tiles
 // instead of nine 128-row ones: on the 8-expert, 8192-row passes the tile
 // count drops to a whole number of waves over the CUs (measured on MI355X:
 // down pass 22 -> 17.7 us; the 64-wide-stage variant when one tile per CU
@@ -235,6 +235,10 @@ static int bf16_tile(const GemmArgs& a) {
   const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
   const int64_t t128 = groups * ((est + 127) / 128) * nt;
   const int64_t t144 = groups * ((est + 143) / 144) * nt;
+  // over several waves of tiles the last wave's share is small and the smaller
+  // tile wastes fewer rows on partly filled groups (capacity-capped ones sit
+  // exactly on 128-row multiples)
+  if (t128 > 4 * kCus) return 128;
   const int64_t cost128 = (t128 + kCus - 1) / kCus * 128;
   const int64_t cost144 = (t144 + kCus - 1) / kCus * 144;
   if (cost144 < cost128) return (t144 <= kCus && gemm_v2_wide_k(a)) ? 145 : 144;
