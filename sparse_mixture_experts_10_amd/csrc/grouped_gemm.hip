@@ -209,8 +209,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 //   0    register-staged kernel (K not a multiple of 32)
 //   64   128 x 64 (narrow N)
 //   128  128 x 128, eight waves
-//   144  144 x 128, six waves, two blocks per CU
-//   145  144 x 128, six waves, 64-wide K stages, one block per CU
+//   144  144 x 128, two blocks per CU (twelve waves and 64-wide K stages, or
+//        six waves and 32-wide stages when K is not a multiple of 64)
+//   145  144 x 128, twelve waves, 64-wide K stages, one block per CU
 //   256  256 x 128, eight waves: many tiles and groups of >= 512 rows
 //   512  256 x 256 with 64-wide K stages: groups of >= 1536 rows (the
 //        weight tiles are re-read from L2 the fewest times; measured on

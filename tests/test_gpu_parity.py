@@ -290,19 +290,21 @@ def test_grouped_gemm_repeatable_full_size(act, G, lo, hi, d, F):
     close_out(np.stack(got), np.stack(want), "bf16", "grouped gemm rows")
 
 
-def test_grouped_gemm_144_row_tiles():
-    """Eight ragged groups averaging 1024 rows at d 512, F 1024 (the default
-    workload's expert passes) take the 144-row tiles: six waves, two blocks a
-    CU on the up pass, 64-wide K stages on the down pass.  Groups of 40 and
-    1851 rows cover a partial tile and a group past eight tiles.  Every row of
-    both passes against a float32 product, the row sums of squares against
-    the float32 activations, and three runs agree bit for bit."""
+@pytest.mark.parametrize("F,with_sq", [(1024, True), (1024, False), (640, False)])
+def test_grouped_gemm_144_row_tiles(F, with_sq):
+    """Eight ragged groups averaging 1024 rows at d 512 (the default workload's
+    expert passes) take the 144-row tiles: two blocks a CU on the up pass (with
+    and without the row sums of squares; F 640 has an odd number of N tiles),
+    64-wide K stages on the down pass.  Groups of 40 and 1851 rows cover a
+    partial tile and a group past eight tiles.  Every row of both passes
+    against a float32 product, the row sums of squares against the float32
+    activations, and three runs agree bit for bit."""
     counts = [1012, 970, 1047, 1160, 40, 1068, 1041, 1851]
-    G, d, F = len(counts), 512, 1024
+    G, d = len(counts), 512
     off = torch.zeros(G + 1, dtype=torch.int32)
     off[1:] = torch.cumsum(torch.tensor(counts), 0)
     rows = int(off[-1])
-    say(f"[gpu] grouped gemm 144-row tiles G={G} rows={rows} d={d} F={F}")
+    say(f"[gpu] grouped gemm 144-row tiles G={G} rows={rows} d={d} F={F} sq={with_sq}")
     g = torch.Generator(device="cuda").manual_seed(8)
     a = torch.randn(rows, d, device="cuda", generator=g).to(torch.bfloat16)
     W1 = (torch.randn(G, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
@@ -316,7 +318,7 @@ def test_grouped_gemm_144_row_tiles():
         hid = torch.zeros(rows, F, dtype=torch.bfloat16, device="cuda")
         sq = torch.zeros(rows, dtype=torch.float32, device="cuda")
         out = torch.zeros(rows, d, dtype=torch.bfloat16, device="cuda")
-        api.moe_expert_up(a, goff, rows, W1, b1, "gelu", hid, sq, ws)
+        api.moe_expert_up(a, goff, rows, W1, b1, "gelu", hid, sq if with_sq else None, ws if with_sq else None)
         api.moe_expert_down(hid, goff, rows, W2, b2, out)
         runs.append((hid, sq, out))
     torch.cuda.synchronize()
@@ -334,7 +336,8 @@ def test_grouped_gemm_144_row_tiles():
         want_sq.append((h * h).sum(1))
         want_o.append(hid[r0:r1].float() @ W2[gi].float().t().contiguous() + b2[gi].float())
     close_out(f64(hid), torch.cat(want_h).double().cpu().numpy(), "bf16", "up pass, 144-row tiles")
-    np.testing.assert_allclose(f64(sq), torch.cat(want_sq).double().cpu().numpy(), rtol=1e-4)
+    if with_sq:
+        np.testing.assert_allclose(f64(sq), torch.cat(want_sq).double().cpu().numpy(), rtol=1e-4)
     close_out(f64(out), torch.cat(want_o).double().cpu().numpy(), "bf16", "down pass, 144-row tiles")
 
 
