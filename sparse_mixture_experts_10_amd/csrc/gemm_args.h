@@ -21,6 +21,7 @@ struct GemmArgs {
   int act;                   // activation, or -1 for none
   float* sq_part;            // [max_rows][n_tiles] partial sum of squares, or nullptr
   bool out_f32;              // C is fp32 (no staging; bias and activation still apply)
+  bool n_major;              // tile order inside a group: N tiles outer (set by the launcher)
 };
 
 }  // namespace moe

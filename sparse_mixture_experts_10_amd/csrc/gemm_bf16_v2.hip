@@ -112,7 +112,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   char* const stages[6] = {st0, st1, st2, st3, st4, st5};
 
   const int n_tiles = (p.N + BN - 1) / BN;
-  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
+  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info, p.n_major);
   if (tl.M <= 0) return;  // uniform
 
   const int tid = threadIdx.x;
@@ -356,6 +356,8 @@ hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
     return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2>(a, st)
                              : launch_v2<144, 128, 3, 2, 3, 1, 2>(a, st);
   if (tile == 145) return launch_v2<144, 128, 3, 4, 4, 2, 1>(a, st);
+  if (tile == 257) return launch_v2<128, 256, 2, 4, 3, 1, 2>(a, st);
+  if (tile == 259) return launch_v2<128, 128, 2, 4, 4, 2, 1>(a, st);
   if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2>(a, st);
   return launch_v2<128, 128, 2, 4, 3, 1, 2>(a, st);
 }

@@ -16,14 +16,16 @@ struct Tile {
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin by id
 constexpr int kCus = 256; // MI355X compute units
 
-// Maps blockIdx.x to a (group, row tile, N tile).  The tile list is row-tile
-// major over the groups in order (so consecutive tiles share A rows and the
-// group's weights) and each XCD takes one contiguous band of it, keeping a
-// band's operands in that XCD's L2.  Wave 0 builds the per-group row-tile
-// prefix from the device-side offsets; the result goes through LDS.
+// Maps blockIdx.x to a (group, row tile, N tile).  The tile list runs over the
+// groups in order; inside a group it is row-tile major (consecutive tiles share
+// A rows) or, with n_major, N-tile major (consecutive tiles share one weight
+// tile: for groups whose weights outweigh their rows).  Each XCD takes one
+// contiguous band of the list, keeping a band's operands in that XCD's L2.
+// Wave 0 builds the per-group row-tile prefix from the device-side offsets;
+// the result goes through LDS.
 template <int BM>
 __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int G, int64_t dense_M, int64_t max_rows,
-                          int n_tiles, int* s_info) {
+                          int n_tiles, int* s_info, bool n_major = false) {
   Tile tl;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -63,6 +65,8 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
       }
     }
     if (work && goff != nullptr) {
+      // group g owns list entries [pre n_tiles, (pre + tiles) n_tiles) in
+      // either order, which is also the row-tile range [pre, pre + tiles)
       int pre = incl - local;
       for (int q = 0; q < gpl; ++q) {
         const int g = g0 + q;
@@ -70,7 +74,12 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
         const int Mg = goff[g + 1] - goff[g];
         const int tiles = (Mg + BM - 1) / BM;
         if (mt >= pre && mt < pre + tiles) {
-          const int r = mt - pre;
+          int r = mt - pre;
+          if (n_major) {
+            const int64_t l = L - (int64_t)pre * n_tiles;
+            r = (int)(l % tiles);
+            s_info[3] = (int)(l / tiles);
+          }
           s_info[0] = g;
           s_info[1] = goff[g] + r * BM;
           s_info[2] = (Mg - r * BM) < BM ? (Mg - r * BM) : BM;

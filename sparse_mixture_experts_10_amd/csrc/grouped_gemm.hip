@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
   __shared__ float s_sq[2][BM];
 
   const int n_tiles = (p.N + BN - 1) / BN;
-  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
+  const Tile tl = find_tile<BM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info, p.n_major);
   if (tl.M <= 0) return;  // uniform
 
   const int tid = threadIdx.x;
@@ -212,6 +212,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 //   144  144 x 128, two blocks per CU (twelve waves and 64-wide K stages, or
 //        six waves and 32-wide stages when K is not a multiple of 64)
 //   145  144 x 128, twelve waves, 64-wide K stages, one block per CU
+//   257  128 x 256, eight waves, two blocks per CU: many waves of tiles,
+//        wide N, K < 2048
+//   259  128 x 128, eight waves, 64-wide K stages and a 4-stage ring, one
+//        block per CU: many waves of tiles, K >= 2048
+//        (measured on MI355X on the switch workload's passes, groups of at
+//        most 256 rows: up, K 1024, 174 -> 156 us; down, K 4096, 174 -> 146 us)
 //   256  256 x 128, eight waves: many tiles and groups of >= 512 rows
 //   512  256 x 256 with 64-wide K stages: groups of >= 1536 rows (the
 //        weight tiles are re-read from L2 the fewest times; measured on
@@ -236,10 +242,15 @@ static int bf16_tile(const GemmArgs& a) {
   const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
   const int64_t t128 = groups * ((est + 127) / 128) * nt;
   const int64_t t144 = groups * ((est + 143) / 144) * nt;
-  // over several waves of tiles the last wave's share is small and the smaller
-  // tile wastes fewer rows on partly filled groups (capacity-capped ones sit
-  // exactly on 128-row multiples)
-  if (t128 > 4 * kCus) return 128;
+  // over several waves of tiles the last wave's share is small and 128 rows
+  // waste fewer rows on partly filled groups (capacity-capped ones sit exactly
+  // on 128-row multiples).  A long K loop takes 64-wide stages and a deep
+  // ring; wide N with a short K loop takes 128 x 256 tiles (64 x 64 a wave).
+  if (t128 > 4 * kCus) {
+    if (a.K >= 2048 && gemm_v2_wide_k(a)) return 259;
+    if (a.N >= 512) return 257;
+    return 128;
+  }
   const int64_t cost128 = (t128 + kCus - 1) / kCus * 128;
   const int64_t cost144 = (t144 + kCus - 1) / kCus * 144;
   if (cost144 < cost128) return (t144 <= kCus && gemm_v2_wide_k(a)) ? 145 : 144;
@@ -248,11 +259,21 @@ static int bf16_tile(const GemmArgs& a) {
 
 int gemm_bf16_n_tiles(const GemmArgs& a) {
   const int t = bf16_tile(a);
-  const int bn = t == 64 ? 64 : t == 512 ? 256 : 128;
+  const int bn = t == 64 ? 64 : (t == 512 || t == 257) ? 256 : 128;
   return (a.N + bn - 1) / bn;
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+// Tile order inside a group: a group's weight tile is read once per row tile,
+// its A rows once per N tile.  When the weights outweigh the rows (N G >
+// rows: small groups, wide layers) the N-major order runs a weight tile's row
+// tiles back to back, so the repeats hit L2.
+static bool gemm_n_major(const GemmArgs& a) {
+  return a.group_offset != nullptr && (int64_t)a.N * a.G > a.max_rows;
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& a0, hipStream_t st) {
+  GemmArgs a = a0;
+  a.n_major = gemm_n_major(a);
   const int t = bf16_tile(a);
   if (t) return launch_gemm_bf16_v2(a, t, st);
   return launch_gemm_bf16_v1(a, st);
@@ -281,7 +302,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   __shared__ int s_info[4];
 
   const int n_tiles = (p.N + FBN - 1) / FBN;
-  const Tile tl = find_tile<FBM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info);
+  const Tile tl = find_tile<FBM>(p.group_offset, p.G, p.dense_M, p.max_rows, n_tiles, s_info, p.n_major);
   if (tl.M <= 0) return;
 
   const int tid = threadIdx.x;
