@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
     double* __restrict__ part) {
   __shared__ int cnt[kGroupChunks][kMaxExperts];
   __shared__ double s_red[256];
+  __shared__ double s_grp[4 * 256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t c = (int64_t)blockIdx.x * kGroupChunks + wave;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(
   if (logits != nullptr) {
     const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
     const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
-    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
+    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1), s_grp);
   }
   __syncthreads();
   if (t < T) {

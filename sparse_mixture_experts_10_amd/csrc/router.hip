@@ -681,64 +681,80 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
 }
 
 // Exact fp64 recomputation of the listed tokens, one token per block at a time.
-// Wave w computes experts w, w + 8, ...: lanes stride the row in float4 chunks
-// (products of bf16 and fp32 are exact in fp64) for two experts at once so
-// plenty of loads are in flight, then wave 0 redoes the epilogue.
-constexpr int kRefineThreads = 512;
+// Exact recomputation of the listed tokens, in two kernels.
+//  * dots: the work items (listed token i, slice of 16 experts) are spread over
+//    the grid; 16 lanes per expert take interleaved float4 chunks of the row
+//    (products of bf16 and fp32 are exact in fp64) with all of a pass's loads
+//    in flight, then sum over the 16 lanes in a fixed order.  h[i][e] (fp64)
+//    goes to the partials buffer, which the finish kernel has consumed.
+//  * epilogue: one wave per listed token redoes the per-token epilogue on h.
+constexpr int kRefineF4 = 16;  // float4 chunks a lane loads per pass (1024 columns a pass)
+
+__global__ __launch_bounds__(256) void router_refine_dots_kernel(
+    const bf16_t* __restrict__ x, int d, const float* __restrict__ Wg, int E,
+    const int32_t* __restrict__ count, const int32_t* __restrict__ list, double* __restrict__ h) {
+  const int n = *count;
+  const int parts = (E + 15) / 16;
+  const int tid = threadIdx.x;
+  const int l = tid & 15;
+  for (int64_t w = blockIdx.x; w < (int64_t)n * parts; w += gridDim.x) {  // uniform
+    const int i = (int)(w / parts);
+    const int e = (int)(w % parts) * 16 + tid / 16;
+    const int64_t t = list[i];
+    double acc = 0.0;
+    if (e < E) {
+      const bf16_t* xr = x + t * (int64_t)d;
+      const float* wr = Wg + (int64_t)e * d;
+      for (int c0 = 0; c0 < d; c0 += 64 * kRefineF4) {
+        float4 wv[kRefineF4];
+        uint2 xv[kRefineF4];  // four bf16
+#pragma unroll
+        for (int q = 0; q < kRefineF4; ++q) {
+          const int col = c0 + (q * 16 + l) * 4;
+          if (col < d) {
+            wv[q] = *(const float4*)(wr + col);
+            xv[q] = *(const uint2*)(xr + col);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kRefineF4; ++q) {
+          const int col = c0 + (q * 16 + l) * 4;
+          if (col < d) {
+            acc = fma((double)__uint_as_float(xv[q].x << 16), (double)wv[q].x, acc);
+            acc = fma((double)__uint_as_float(xv[q].x & 0xffff0000u), (double)wv[q].y, acc);
+            acc = fma((double)__uint_as_float(xv[q].y << 16), (double)wv[q].z, acc);
+            acc = fma((double)__uint_as_float(xv[q].y & 0xffff0000u), (double)wv[q].w, acc);
+          }
+        }
+      }
+    }
+    acc += xor_lane_d<1>(acc);
+    acc += xor_lane_d<2>(acc);
+    acc += xor_lane_d<4>(acc);
+    acc += xor_lane_d<8>(acc);
+    if (l == 0 && e < E) h[(int64_t)i * E + e] = acc;
+  }
+}
 
 template <int EP>
-__global__ __launch_bounds__(kRefineThreads) void router_refine_kernel(
-    const bf16_t* __restrict__ x, int d, const float* __restrict__ Wg, const float* __restrict__ bg,
-    const float* __restrict__ bsel, int E, int k, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ list, float* __restrict__ logits, float* __restrict__ lse_out,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, const float* __restrict__ noise,
-    double sigma) {
+__global__ __launch_bounds__(256) void router_refine_epilogue_kernel(
+    const double* __restrict__ h, const float* __restrict__ bg, const float* __restrict__ bsel, int E,
+    int k, const int32_t* __restrict__ count, const int32_t* __restrict__ list,
+    float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
   constexpr int TE = (EP + 63) / 64;
-  constexpr int NWAVE = kRefineThreads / 64;
-  __shared__ double s_h[EP];
-  extern __shared__ float s_x[];  // one token row, fp32
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = *count;
-  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = blockIdx.x * 4 + wave; i < n; i += gridDim.x * 4) {  // uniform per wave
     const int64_t t = list[i];
-    for (int j = tid; j < d; j += kRefineThreads) s_x[j] = bf16_to_f32(x[t * (int64_t)d + j]);
-    __syncthreads();
-    for (int e0 = wave; e0 < E; e0 += 2 * NWAVE) {
-      const int e1 = e0 + NWAVE;
-      const float4* w0 = (const float4*)(Wg + (int64_t)e0 * d);
-      const float4* w1 = (const float4*)(Wg + (int64_t)(e1 < E ? e1 : e0) * d);
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll 4
-      for (int q = lane; q < d / 4; q += 64) {
-        const float4 u = w0[q], v = w1[q];
-        const float4 xv = ((const float4*)s_x)[q];
-        a0 = fma((double)xv.x, (double)u.x, a0); a0 = fma((double)xv.y, (double)u.y, a0);
-        a0 = fma((double)xv.z, (double)u.z, a0); a0 = fma((double)xv.w, (double)u.w, a0);
-        a1 = fma((double)xv.x, (double)v.x, a1); a1 = fma((double)xv.y, (double)v.y, a1);
-        a1 = fma((double)xv.z, (double)v.z, a1); a1 = fma((double)xv.w, (double)v.w, a1);
-      }
+    double acc[TE];
 #pragma unroll
-      for (int m = 32; m > 0; m >>= 1) {
-        a0 += __shfl_xor(a0, m, 64);
-        a1 += __shfl_xor(a1, m, 64);
-      }
-      if (lane == 0) {
-        s_h[e0] = a0;
-        if (e1 < E) s_h[e1] = a1;
-      }
+    for (int j = 0; j < TE; ++j) {
+      const int e = lane + 64 * j;
+      acc[j] = e < E ? h[(int64_t)i * E + e] : 0.0;
     }
-    __syncthreads();
-    if (wave == 0) {
-      double acc[TE];
-#pragma unroll
-      for (int j = 0; j < TE; ++j) {
-        const int e = lane + 64 * j;
-        acc[j] = e < E ? s_h[e] : 0.0;
-      }
-      token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                             noise, sigma);
-    }
-    __syncthreads();
+    token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
+                           noise, sigma);
   }
 }
 
@@ -779,10 +795,13 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   const int64_t tpb = 256 / NXE;
   hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
                      part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma);
-  const unsigned nref = (unsigned)(T < 1024 ? T : 1024);
-  hipLaunchKernelGGL((router_refine_kernel<EP>), dim3(nref), dim3(kRefineThreads), (size_t)d * sizeof(float),
-                     st, (const bf16_t*)x, d, Wg, bg, bsel, E, k, count, list, logits, lse, idx, gate,
-                     noise, sigma);
+  // the listed tokens' exact logits go into the consumed partials buffer
+  // (T E doubles <= T 3E floats)
+  double* h = (double*)part;
+  hipLaunchKernelGGL(router_refine_dots_kernel, dim3(1024), dim3(256), 0, st, (const bf16_t*)x, d, Wg, E,
+                     count, list, h);
+  hipLaunchKernelGGL((router_refine_epilogue_kernel<EP>), dim3(256), dim3(256), 0, st, h, bg, bsel, E, k,
+                     count, list, logits, lse, idx, gate, noise, sigma);
   return hipGetLastError();
 }
 

@@ -31,9 +31,10 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
     float* __restrict__ credit, double* __restrict__ part, float* __restrict__ credit_row,
     const float* __restrict__ token_loss, float* __restrict__ loss_row) {
   __shared__ double s_red[256];
+  __shared__ double s_grp[4 * 256];
   const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
   const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
-  stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1));
+  stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1), s_grp);
   const int64_t t = t0 + threadIdx.x;
   if (credit != nullptr && t < t1) {
     for (int j = 0; j < k; ++j) {

@@ -19,13 +19,15 @@ namespace moe {
 constexpr int kStatsSubs = kStatsTokens / kStatsSub;  // sub-partials per group
 
 // One 256-thread block: the group value of tokens [t0, t1) (t1 - t0 <= 256):
-// softmax mass per expert into out[0..E-1], lse^2 into out[E].  Experts go in
-// rounds of 16: thread (i, el) sums sub-block i of expert e0 + el.
-// s_red: 256 doubles.
+// softmax mass per expert into out[0..E-1], lse^2 into out[E].  Thread
+// (i, el) sums sub-block i of experts e0 + el, e0 + 16 + el, ... for up to four
+// rounds of 16 experts whose loads are all issued before any wait (64 experts
+// a pass).  s_red: 256 doubles; s_grp: 4 * 256 doubles.
 __device__ __forceinline__ void stats_block_partials(const float* __restrict__ logits,
                                                      const float* __restrict__ lse, int64_t t0,
                                                      int64_t t1, int E, double* s_red,
-                                                     double* __restrict__ out) {
+                                                     double* __restrict__ out, double* s_grp) {
+  constexpr int R = 4;  // expert rounds per pass
   const int tid = threadIdx.x;
   const int i = tid / kStatsSub, el = tid % kStatsSub;   // sub-block, expert in the round
   const int64_t s0 = t0 + (int64_t)i * kStatsSub;
@@ -33,23 +35,30 @@ __device__ __forceinline__ void stats_block_partials(const float* __restrict__ l
   float l[kStatsSub];
 #pragma unroll
   for (int u = 0; u < kStatsSub; ++u) l[u] = u < n ? lse[s0 + u] : 0.f;
-  for (int e0 = 0; e0 < E; e0 += kStatsSub) {
-    const int e = e0 + el;
-    double m = 0.0;
-    if (e < E) {
-      float h[kStatsSub];
+  for (int e0 = 0; e0 < E; e0 += R * kStatsSub) {
+    float h[R][kStatsSub];
 #pragma unroll
-      for (int u = 0; u < kStatsSub; ++u) h[u] = u < n ? logits[(s0 + u) * E + e] : 0.f;
+    for (int r = 0; r < R; ++r) {
+      const int e = e0 + r * kStatsSub + el;
+#pragma unroll
+      for (int u = 0; u < kStatsSub; ++u) h[r][u] = (u < n && e < E) ? logits[(s0 + u) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      double m = 0.0;
 #pragma unroll
       for (int u = 0; u < kStatsSub; ++u)
-        if (u < n) m += (double)expf(h[u] - l[u]);
+        if (u < n) m += (double)expf(h[r][u] - l[u]);
+      s_grp[r * 256 + tid] = m;
     }
-    s_red[tid] = m;
     __syncthreads();
-    if (tid < kStatsSub && e0 + tid < E) {
-      double g = 0.0;
-      for (int q = 0; q < kStatsSubs; ++q) g += s_red[q * kStatsSub + tid];
-      out[e0 + tid] = g;
+    if (tid < R * kStatsSub) {
+      const int r = tid / kStatsSub, e = e0 + tid;
+      if (e < E) {
+        double g = 0.0;
+        for (int q = 0; q < kStatsSubs; ++q) g += s_grp[r * 256 + q * kStatsSub + (tid % kStatsSub)];
+        out[e] = g;
+      }
     }
     __syncthreads();
   }
