@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const vec16* __restrict__ 
 #pragma unroll
       for (int u = 0; u < 4; ++u) o.w[u] = __float_as_uint(acc[u]);
     }
-    y[t * vpr + v] = o;
+    store16_agent(y + t * vpr + v, o);
   }
 }
 

@@ -16,6 +16,20 @@ struct alignas(16) vec16 {
   uint32_t w[4];
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global store at agent scope (sc1).  On MI355X a plain store leaves
+// the line dirty in this XCD's L2 until the write-back at the end of the
+// kernel, which then runs after the last wave; an agent-scope store writes
+// the line through as it is issued, so a pass's output drains while other
+// blocks still compute (measured on the 8-expert default layer: expert up
+// pass 19.2 -> 17.9 us, down pass 16.0 -> 15.0 us, combine 3.7 -> 3.4 us).
+// Same bytes, and the end-of-kernel release still orders them.
+__device__ __forceinline__ void store16_agent(void* dst, const vec16& v) {
+  const u32x4_t q = {v.w[0], v.w[1], v.w[2], v.w[3]};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(q) : "memory");
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

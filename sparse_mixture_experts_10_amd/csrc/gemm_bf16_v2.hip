@@ -293,7 +293,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
       const int m = (sr >> 4) * C::WM + i * 16 + (sr & 15);
       const int n = n0 + cv * 8;
       if (m < tl.M && n < N)
-        *(vec16*)(Cg + (tl.row0 + m) * (int64_t)N + n) = *(const vec16*)(Cs + sr * C::LDC + cv * 8);
+        store16_agent(Cg + (tl.row0 + m) * (int64_t)N + n, *(const vec16*)(Cs + sr * C::LDC + cv * 8));
     }
     __syncthreads();
   }
