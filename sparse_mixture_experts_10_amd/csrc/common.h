@@ -10,6 +10,8 @@ typedef uint16_t bf16_t;  // bf16 stored as its 16-bit pattern
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // 16 bytes moved as one unit (8 bf16 or 4 fp32).
 struct alignas(16) vec16 {
@@ -49,11 +51,17 @@ __device__ __forceinline__ void unpack_bf16x8(const vec16& v, float* f) {
   }
 }
 
+// Two fp32 -> two bf16 in one dword (low half first): one v_cvt_pk_bf16_f32,
+// the same rounding as f32_to_bf16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 __device__ __forceinline__ vec16 pack_bf16x8(const float* f) {
   vec16 v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v.w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) v.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
   return v;
 }
 
@@ -63,20 +71,25 @@ enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWISH = 2 };
 // erf(z / sqrt 2) = sign(z) (1 - erfc(|z| / sqrt 2)), this is
 //   GELU(z) = max(z, 0) - 0.5 |z| erfc(|z| / sqrt 2).
 // erfc(x) for x >= 0 by Abramowitz & Stegun 7.1.26 (t = 1 / (1 + p x),
-// erfc = t (a1 + t (a2 + ...)) e^{-x^2}, |error| <= 1.5e-7), with the hardware
-// reciprocal and exp2 and x = |z| / sqrt 2 folded into the constants
-// (p x = (p / sqrt 2) |z|, x^2 log2(e) = z^2 log2(e) / 2): 12 VALU
-// instructions and two transcendentals.
+// erfc = t (a1 + t (a2 + ...)) e^{-x^2}, |error| <= 1.5e-7), evaluated on
+// s = z / sqrt(2 ln 2), so that e^{-x^2} = 2^{-s^2} (the hardware exp2) and
+// 0.5 |z| = sqrt(ln 2 / 2) |s|, with the polynomial made monic and its
+// leading coefficient a5 sqrt(ln 2 / 2) = 2^-L moved into the exponent:
+//   GELU(z) = max(z, 0) - |s| t (c0 + t (c1 + t (c2 + t (c3 + t)))) 2^{-(s^2 + L)},
+//   t = 1 / (1 + p sqrt(ln 2) |s|),  c_i = a_{i+1} / a5.
+// Twelve VALU instructions with the bias add and no constant moves (every
+// literal lands in an instruction that takes one), plus two transcendentals.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float az = fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188826636f, az, 1.0f));  // p / sqrt 2
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);  // e^{-z^2 / 2}
-  const float q = p * t * e;                                               // erfc(|z| / sqrt 2)
-  return fmaf(-0.5f * az, q, fmaxf(z, 0.0f));
+  const float s = z * 0.84932180028801907f;  // 1 / sqrt(2 ln 2)
+  const float as = fabsf(s);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.27273748088f, as, 1.0f));
+  float h = t + -1.3690829039f;
+  h = fmaf(h, t, 1.3391807712f);
+  h = fmaf(h, t, -0.26803776222f);
+  h = fmaf(h, t, 0.24008694985f);
+  h *= t;
+  const float e = __builtin_amdgcn_exp2f(-fmaf(s, s, 0.67840735333f));
+  return fmaf(-as, h * e, fmaxf(z, 0.0f));
 }
 
 // Swish / SiLU z sigmoid(z) = z / (1 + e^{-z}), with the hardware exp2 and

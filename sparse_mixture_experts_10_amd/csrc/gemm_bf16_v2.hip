@@ -33,6 +33,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waits until at most min(ahead, M) groups of G loads are outstanding
+// (ahead: a wave-uniform count, so the branches are scalar).
+template <int M, int G>
+__device__ __forceinline__ void wait_vmcnt_groups(int ahead) {
+  if constexpr (M == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= M) wait_vmcnt<M * G>();
+    else wait_vmcnt_groups<M - 1, G>(ahead);
+  }
+}
+
 // Stage rows are 64 SUB bytes (32 SUB bf16 of K) with their 16-byte chunks
 // permuted: logical chunk c of row r sits at chunk c ^ swz(r).  The LDS serves
 // a ds_read_b128 eight lanes at a time from 128 bytes of banks, so the eight
@@ -147,7 +159,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   }
   const int nk = K / C::KS;
   auto issue = [&](int kt, int stage) {
-    const int k = (kt < nk ? kt : nk - 1) * C::KS;  // past the end: harmless reload
+    const int k = kt * C::KS;
     char* base = stages[stage];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -187,12 +199,16 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   }
 
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
 
+  // Only stages below nk are loaded: at step kt the stages after kt still in
+  // flight number min(NS - 2, nk - 1 - kt), so the wait shrinks in the last
+  // steps instead of the ring reloading past the end.
   auto step = [&](int kt, int stage) {
-    wait_vmcnt<(NS - 2) * LPW>();   // this wave's loads of stage kt have landed
-    slab_barrier();                  // ... and every other wave's
-    issue(kt + NS - 1, (stage + NS - 1) % NS);
+    wait_vmcnt_groups<NS - 2, LPW>(nk - 1 - kt);  // this wave's loads of stage kt have landed
+    slab_barrier();                                // ... and every other wave's
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (stage + NS - 1) % NS);
     const char* base = stages[stage];
 #pragma unroll
     for (int h = 0; h < SUB; ++h) {
@@ -205,7 +221,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -220,41 +236,47 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- epilogue: lane holds C[wm*WM + i*16 + 4*fc + r][wn*WN + j*16 + fr] ----
+  // ---- epilogue: lane holds C[wm*WM + i*16 + fr][wn*WN + j*16 + 4*fc + r] ----
+  // (the weight operand goes first, so each lane holds four consecutive
+  // columns of one row; N % 8 == 0 puts all four in range or none)
   const bf16_t* bias = (const bf16_t*)p.bias;
-  float bcol[TN];
+  float bcol[TN][4];
   bool ncol_ok[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * C::WN + j * 16 + fr;
+    const int n = n0 + wn * C::WN + j * 16 + fc * 4;
     ncol_ok[j] = n < N;
-    float bv = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bcol[j][r] = 0.f;
     if (ncol_ok[j] && bias != nullptr) {
       if (SEG) {
-        for (int q = 0; q < p.S; ++q) bv += bf16_to_f32(bias[(int64_t)q * N + n]);
+        for (int q = 0; q < p.S; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bcol[j][r] += bf16_to_f32(bias[(int64_t)q * N + n + r]);
       } else {
-        bv = bf16_to_f32(bias[(int64_t)tl.g * N + n]);
+        const uint2 bb = *(const uint2*)(bias + (int64_t)tl.g * N + n);
+        bcol[j][0] = __uint_as_float(bb.x << 16);
+        bcol[j][1] = __uint_as_float(bb.x & 0xffff0000u);
+        bcol[j][2] = __uint_as_float(bb.y << 16);
+        bcol[j][3] = __uint_as_float(bb.y & 0xffff0000u);
       }
     }
-    bcol[j] = bv;
   }
   const bool want_sq = p.sq_part != nullptr;
   if (p.out_f32) {
-    // fp32 result straight from the accumulators (each 16 lanes store 64
-    // contiguous bytes of one row)
+    // fp32 result straight from the accumulators: 16 contiguous bytes a lane
     float* Cf = (float*)p.C;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        const int m = wm * C::WM + i * 16 + fr;
+        const int n = n0 + wn * C::WN + j * 16 + fc * 4;
+        f32x4_t v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = wm * C::WM + i * 16 + fc * 4 + r;
-          const int n = n0 + wn * C::WN + j * 16 + fr;
-          float v = acc[i][j][r] + bcol[j];
-          v = act_static<ACT>(v);
-          if (m < tl.M && n < N) Cf[(tl.row0 + m) * (int64_t)N + n] = v;
-        }
+        for (int r = 0; r < 4; ++r) v[r] = act_static<ACT>(acc[i][j][r] + bcol[j][r]);
+        if (m < tl.M && ncol_ok[j]) *(f32x4_t*)(Cf + (tl.row0 + m) * (int64_t)N + n) = v;
+      }
     return;
   }
   bf16_t* Cs = (bf16_t*)st0;
@@ -264,26 +286,25 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   // 16 * wm + q holds tile row wm * WM + 16 i + q) and stores them
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs = 0.f;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
+      float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = act_static<ACT>(acc[i][j][r] + bcol[j]);
-        if (want_sq && ncol_ok[j]) rs[r] += v * v;
-        Cs[(wm * 16 + fc * 4 + r) * C::LDC + wn * C::WN + j * 16 + fr] = f32_to_bf16(v);
+        v[r] = act_static<ACT>(acc[i][j][r] + bcol[j][r]);
+        if (want_sq && ncol_ok[j]) rs += v[r] * v[r];
       }
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *(uint2*)(Cs + (wm * 16 + fr) * C::LDC + wn * C::WN + j * 16 + fc * 4) = pk;
     }
     if (want_sq) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sum = rs[r];
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 2, 64);
-        sum += __shfl_xor(sum, 4, 64);
-        sum += __shfl_xor(sum, 8, 64);
-        if (fr == 0) s_sq[wn][wm * C::WM + i * 16 + fc * 4 + r] = sum;
-      }
+      // the row's 4 fc lanes, then (below) the WGN wave columns in order
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      if (fc == 0) s_sq[wn][wm * C::WM + i * 16 + fr] = rs;
     }
     __syncthreads();
     constexpr int VPR = BN / 8;  // 16-byte vectors per staged row
