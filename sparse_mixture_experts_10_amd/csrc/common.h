@@ -27,9 +27,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // blocks still compute (measured on the 8-expert default layer: expert up
 // pass 19.2 -> 17.9 us, down pass 16.0 -> 15.0 us, combine 3.7 -> 3.4 us).
 // Same bytes, and the end-of-kernel release still orders them.
+// A VALU write to the data VGPRs of a store wider than 8 bytes must come at
+// least two wait states after the store on gfx950; the compiler inserts them
+// after its own stores but cannot see into inline asm, so the s_nop 1 is part
+// of the asm (without it a following VALU may overwrite the data before the
+// store reads it, corrupting 16-byte chunks now and then).
 __device__ __forceinline__ void store16_agent(void* dst, const vec16& v) {
   const u32x4_t q = {v.w[0], v.w[1], v.w[2], v.w[3]};
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(q) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(q) : "memory");
 }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {

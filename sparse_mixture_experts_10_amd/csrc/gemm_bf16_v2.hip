@@ -33,18 +33,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Waits until at most min(ahead, M) groups of G loads are outstanding
-// (ahead: a wave-uniform count, so the branches are scalar).
-template <int M, int G>
-__device__ __forceinline__ void wait_vmcnt_groups(int ahead) {
-  if constexpr (M == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (ahead >= M) wait_vmcnt<M * G>();
-    else wait_vmcnt_groups<M - 1, G>(ahead);
-  }
-}
-
 // Stage rows are 64 SUB bytes (32 SUB bf16 of K) with their 16-byte chunks
 // permuted: logical chunk c of row r sits at chunk c ^ swz(r).  The LDS serves
 // a ds_read_b128 eight lanes at a time from 128 bytes of banks, so the eight
@@ -159,7 +147,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   }
   const int nk = K / C::KS;
   auto issue = [&](int kt, int stage) {
-    const int k = kt * C::KS;
+    const int k = (kt < nk ? kt : nk - 1) * C::KS;  // past the end: harmless reload
     char* base = stages[stage];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -199,16 +187,12 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   }
 
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
-  // Only stages below nk are loaded: at step kt the stages after kt still in
-  // flight number min(NS - 2, nk - 1 - kt), so the wait shrinks in the last
-  // steps instead of the ring reloading past the end.
   auto step = [&](int kt, int stage) {
-    wait_vmcnt_groups<NS - 2, LPW>(nk - 1 - kt);  // this wave's loads of stage kt have landed
-    slab_barrier();                                // ... and every other wave's
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (stage + NS - 1) % NS);
+    wait_vmcnt<(NS - 2) * LPW>();   // this wave's loads of stage kt have landed
+    slab_barrier();                  // ... and every other wave's
+    issue(kt + NS - 1, (stage + NS - 1) % NS);
     const char* base = stages[stage];
 #pragma unroll
     for (int h = 0; h < SUB; ++h) {

@@ -30,14 +30,22 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int total_m, incl = 0, local = 0, g0 = 0, gpl = 1;
+    int gs[4], gm[4];  // start and rows of this lane's groups, kept for the owner search
     if (goff == nullptr) {
       total_m = (int)((dense_M + BM - 1) / BM);
     } else {
-      gpl = (G + 63) / 64;  // groups per lane (<= 4)
+      gpl = (G + 63) / 64;  // groups per lane (<= 4: at most 256 groups)
       g0 = lane * gpl;
-      for (int q = 0; q < gpl; ++q) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const int g = g0 + q;
-        if (g < G) local += (goff[g + 1] - goff[g] + BM - 1) / BM;
+        gs[q] = 0;
+        gm[q] = 0;
+        if (q < gpl && g < G) {
+          gs[q] = goff[g];
+          gm[q] = goff[g + 1] - gs[q];
+        }
+        local += (gm[q] + BM - 1) / BM;
       }
       incl = local;
 #pragma unroll
@@ -68,11 +76,11 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
       // group g owns list entries [pre n_tiles, (pre + tiles) n_tiles) in
       // either order, which is also the row-tile range [pre, pre + tiles)
       int pre = incl - local;
-      for (int q = 0; q < gpl; ++q) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const int g = g0 + q;
-        if (g >= G) break;
-        const int Mg = goff[g + 1] - goff[g];
-        const int tiles = (Mg + BM - 1) / BM;
+        const int Mg = gm[q];
+        const int tiles = (Mg + BM - 1) / BM;  // 0 past this lane's groups
         if (mt >= pre && mt < pre + tiles) {
           int r = mt - pre;
           if (n_major) {
@@ -81,7 +89,7 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
             s_info[3] = (int)(l / tiles);
           }
           s_info[0] = g;
-          s_info[1] = goff[g] + r * BM;
+          s_info[1] = gs[q] + r * BM;
           s_info[2] = (Mg - r * BM) < BM ? (Mg - r * BM) : BM;
         }
         pre += tiles;
