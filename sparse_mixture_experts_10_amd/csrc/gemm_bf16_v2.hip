@@ -352,10 +352,16 @@ bool gemm_v2_wide_k(const GemmArgs& a) { return a.K % 64 == 0 && (a.S <= 1 || a.
 // the 8-expert default passes: up 23.9 -> 20.2 us, down 17.8 -> 16.2 us
 // against six waves in 3 x 2; the extra waves hide the LDS and load latency
 // that one or two six-wave blocks leave exposed).  Without 64-wide K they use
-// six waves in 3 x 2 and 32-wide stages.  Every configuration accumulates K
-// in the same order, so all give the same bits.
+// six waves in 3 x 2 and 32-wide stages.  Over several waves of 256 x 256
+// tiles a 4-stage ring of 32-wide stages (128 KB) keeps three stages of loads
+// in flight where the 2-stage 64-wide ring keeps one (measured on MI355X: 128
+// experts of 2048 rows at d 4096, F 1536: up 3646 -> 3284 us, down 3677 ->
+// 3449 us; 64 experts of 768 rows at d 2048, F 1408: down 380 -> 350 us).
+// Every configuration accumulates K in the same order, so all give the same
+// bits.
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   if (tile == 512) return launch_v2<256, 256, 2, 4, 2, 2, 1>(a, st);
+  if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2>(a, st);
   if (tile == 144)
     return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2>(a, st)

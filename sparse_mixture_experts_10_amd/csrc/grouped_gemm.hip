@@ -234,12 +234,16 @@ static int bf16_tile(const GemmArgs& a) {
   if (a.N <= 64) return 64;
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
   const int64_t per_group = a.group_offset ? rows / a.G : rows;
+  const int64_t groups = a.group_offset ? a.G : 1;
+  const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
+  // several waves of 256 x 256 tiles: the 32-wide 4-stage ring keeps three
+  // stages of loads in flight behind the MFMAs
+  const int64_t t256 = groups * ((est + 255) / 256) * ((a.N + 255) / 256);
+  if (a.N >= 256 && per_group >= 512 && t256 >= 4 * kCus) return 513;
   if (gemm_v2_wide_k(a) && a.N >= 512 && per_group >= 1536) return 512;
   const int64_t big = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 127) / 128);
   if (big >= 1024 && per_group >= 512) return 256;
   const int64_t nt = (a.N + 127) / 128;
-  const int64_t groups = a.group_offset ? a.G : 1;
-  const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
   const int64_t t128 = groups * ((est + 127) / 128) * nt;
   const int64_t t144 = groups * ((est + 143) / 144) * nt;
   // over several waves of tiles the last wave's share is small and 128 rows
@@ -259,7 +263,7 @@ static int bf16_tile(const GemmArgs& a) {
 
 int gemm_bf16_n_tiles(const GemmArgs& a) {
   const int t = bf16_tile(a);
-  const int bn = t == 64 ? 64 : (t == 512 || t == 257) ? 256 : 128;
+  const int bn = t == 64 ? 64 : (t == 512 || t == 513 || t == 257) ? 256 : 128;
   return (a.N + bn - 1) / bn;
 }
 

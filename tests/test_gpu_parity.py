@@ -246,16 +246,18 @@ def test_grouped_ffn_ragged_groups(dtype, d, gather):
 
 
 @pytest.mark.parametrize("act,G,lo,hi,d,F", [("swish", 64, 596, 988, 2048, 1408), (None, 64, 596, 988, 2048, 1408),
-                                              ("gelu", 16, 1800, 2300, 1024, 1536),
+                                              ("gelu", 16, 1800, 2300, 1024, 1536), ("relu", 48, 560, 640, 1024, 1536),
                                               ("relu", 64, 60, 257, 1024, 4096), (None, 96, 60, 257, 4096, 1024)])
 def test_grouped_gemm_repeatable_full_size(act, G, lo, hi, d, F):
-    """The expert-up pass at full expert shapes (the fine-grained workload's 64
-    ragged groups of ~768 rows, d 2048, F 1408; 16 groups of ~2048 rows, which
-    take the 256 x 256 tiles; and the switch workload's groups of at most 256
-    rows at N 4096, K 1024 (128 x 256 tiles) and at N 1024, K 4096 (64-wide K
-    stages in a 4-stage ring)), run three times: the outputs agree bit for
-    bit.  Guards the LDS
-    stage ring against reads racing the refill of their stage (such a race
+    """The expert-up pass at full expert shapes, run three times: the outputs
+    agree bit for bit.  The shapes cover each large tile: the fine-grained
+    workload's 64 ragged groups of ~768 rows at d 2048, F 1408 (256 x 256
+    tiles, 32-wide K stages in a 4-stage ring); 16 groups of ~2048 rows (256 x
+    256 tiles, 64-wide stages in a 2-stage ring); 48 groups of ~600 rows at
+    d 1024, F 1536 (256 x 128 tiles, two blocks a CU); and the switch
+    workload's groups of at most 256 rows at N 4096, K 1024 (128 x 256 tiles)
+    and at N 1024, K 4096 (64-wide K stages in a 4-stage ring).  Guards the
+    LDS stage ring against reads racing the refill of their stage (such a race
     corrupts a few scattered 16-byte chunks)."""
     counts = torch.randint(lo, hi, (G,), generator=torch.Generator().manual_seed(5))
     off = torch.zeros(G + 1, dtype=torch.int32)
