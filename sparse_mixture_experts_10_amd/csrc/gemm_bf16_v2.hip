@@ -101,6 +101,8 @@ __attribute__((amdgpu_waves_per_eu(MINB * ((WGM * WGN + 3) / 4))))
 void gemm_bf16_v2_kernel(GemmArgs p) {
   using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG>;
   constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
+  // ping-pong schedule (two groups of four waves, one of each a SIMD)
+  constexpr bool PP = BM == 256 && BN == 256 && WGM == 2 && WGN == 4 && NS == 4 && SUB == 1;
   __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
   __shared__ __attribute__((aligned(1024))) char st1[C::SLAB];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? C::SLAB : 16];
@@ -186,6 +188,57 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     }
   }
 
+  if constexpr (PP) {
+    // Ping-pong: waves 0-3 (group 0) and 4-7 (group 1) put one wave of each
+    // group on every SIMD.  Every wave runs the same loop, per stage j:
+    //   MEM(j): refill stage j - 1's buffer with this wave's share of stage
+    //           j + NS - 1, read stage j's operands, wait for its share of
+    //           stage j + 1; barrier
+    //   MUL(j): multiply stage j; barrier
+    // and group 1 passes one extra barrier before the loop (group 0 one
+    // after it), so barrier arrivals pair group 0's MUL with group 1's MEM
+    // and the other way round: one wave a SIMD multiplies while the other
+    // loads and reads.  Stage j is read by group 0 between barriers 2j and
+    // 2j + 1 and by group 1 between 2j + 1 and 2j + 2, so its buffer is free
+    // from barrier 2j + 2, where both groups' MEM(j + 1) start; every share of
+    // stage j + 1 is waited for before barrier 2j + 1 (group 0) or 2j + 2
+    // (group 1), ahead of both groups' reads of it.
+    const int grp = wave >> 2;
+    bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s, s);
+    wait_vmcnt<(NS - 2) * LPW>();  // stage 0
+    slab_barrier();
+    if (grp == 1) slab_barrier();
+    auto pp_step = [&](int kt, int stage) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kt + NS - 1, (stage + NS - 1) % NS);
+      const char* base = stages[stage];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = *(const bf16x8_t*)(base + a_rd[0][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = *(const bf16x8_t*)(base + b_rd[0][j]);
+      wait_vmcnt<(NS - 2) * LPW>();  // this wave's share of stage kt + 1
+      slab_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      slab_barrier();
+    };
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pp_step(kt + s, s);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (kt + s < nk) pp_step(kt + s, s);
+    if (grp == 0) slab_barrier();
+  } else {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
@@ -217,6 +270,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (kt + s < nk) step(kt + s, s);
+  }
   wait_vmcnt<0>();
   __syncthreads();
 
