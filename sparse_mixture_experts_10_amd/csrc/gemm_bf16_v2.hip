@@ -414,7 +414,6 @@ bool gemm_v2_wide_k(const GemmArgs& a) { return a.K % 64 == 0 && (a.S <= 1 || a.
 // Every configuration accumulates K in the same order, so all give the same
 // bits.
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
-  if (tile == 512) return launch_v2<256, 256, 2, 4, 2, 2, 1>(a, st);
   if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2>(a, st);
   if (tile == 144)

@@ -219,9 +219,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 //        (measured on MI355X on the switch workload's passes, groups of at
 //        most 256 rows: up, K 1024, 174 -> 156 us; down, K 4096, 174 -> 146 us)
 //   256  256 x 128, eight waves: many tiles and groups of >= 512 rows
-//   512  256 x 256 with 64-wide K stages: groups of >= 1536 rows (the
-//        weight tiles are re-read from L2 the fewest times; measured on
-//        MI355X 3-9 % faster than 256 x 128 on the largest expert shapes)
+//   513  256 x 256, eight waves in two ping-pong groups, 32-wide K stages in
+//        a 4-stage ring: groups of >= 512 rows over four or more waves of
+//        tiles, or groups of >= 1536 rows (the weight tiles are re-read from
+//        L2 the fewest times; measured on MI355X against the 64-wide 2-stage
+//        ring it replaces: the two shared experts of the fine-grained layer,
+//        d 2048, F 1408, 8192 rows, 218 -> 186 us)
 // Between 128 and 144 rows, for passes of at most four waves of 128-row tiles,
 // the one that puts the fewest rows on the busiest CU wins, with every group
 // assumed to hold its mean share plus 8 % (routing imbalance).  A group of up to 1152 rows then takes eight 144-row tiles
@@ -236,11 +239,11 @@ static int bf16_tile(const GemmArgs& a) {
   const int64_t per_group = a.group_offset ? rows / a.G : rows;
   const int64_t groups = a.group_offset ? a.G : 1;
   const int64_t est = a.group_offset ? (per_group * 108 + 99) / 100 : rows;
-  // several waves of 256 x 256 tiles: the 32-wide 4-stage ring keeps three
-  // stages of loads in flight behind the MFMAs
+  // 256 x 256 tiles (32-wide 4-stage ring, ping-pong waves) for several
+  // waves of tiles or for groups of 1536 rows and more
   const int64_t t256 = groups * ((est + 255) / 256) * ((a.N + 255) / 256);
   if (a.N >= 256 && per_group >= 512 && t256 >= 4 * kCus) return 513;
-  if (gemm_v2_wide_k(a) && a.N >= 512 && per_group >= 1536) return 512;
+  if (a.N >= 512 && per_group >= 1536) return 513;
   const int64_t big = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 127) / 128);
   if (big >= 1024 && per_group >= 512) return 256;
   const int64_t nt = (a.N + 127) / 128;
@@ -263,7 +266,7 @@ static int bf16_tile(const GemmArgs& a) {
 
 int gemm_bf16_n_tiles(const GemmArgs& a) {
   const int t = bf16_tile(a);
-  const int bn = t == 64 ? 64 : (t == 512 || t == 513 || t == 257) ? 256 : 128;
+  const int bn = t == 64 ? 64 : (t == 513 || t == 257) ? 256 : 128;
   return (a.N + bn - 1) / bn;
 }
 

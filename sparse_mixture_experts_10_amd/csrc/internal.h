@@ -75,7 +75,7 @@ int gemm_bf16_n_tiles(const GemmArgs& a);                           // N tiles o
 hipError_t launch_gemm_bf16_v1(const GemmArgs& a, hipStream_t st);  // any K % 8 == 0
 bool gemm_v2_supported(const GemmArgs& a);                         // K % 32 == 0
 bool gemm_v2_wide_k(const GemmArgs& a);                            // K % 64 == 0
-hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st);  // tile 64, 128, 144, 145, 257, 259, 256, 512, 513
+hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st);  // tile 64, 128, 144, 145, 257, 259, 256, 513
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_sq_reduce(const float* sq_part, int n_tiles, const int32_t* group_offset, int G,
                             int64_t max_rows, float* sq, hipStream_t st);

@@ -251,9 +251,9 @@ def test_grouped_ffn_ragged_groups(dtype, d, gather):
 def test_grouped_gemm_repeatable_full_size(act, G, lo, hi, d, F):
     """The expert-up pass at full expert shapes, run three times: the outputs
     agree bit for bit.  The shapes cover each large tile: the fine-grained
-    workload's 64 ragged groups of ~768 rows at d 2048, F 1408 (256 x 256
-    tiles, 32-wide K stages in a 4-stage ring); 16 groups of ~2048 rows (256 x
-    256 tiles, 64-wide stages in a 2-stage ring); 48 groups of ~600 rows at
+    workload's 64 ragged groups of ~768 rows at d 2048, F 1408 and 16 groups
+    of ~2048 rows (256 x 256 tiles, ping-pong waves, 32-wide K stages in a
+    4-stage ring); 48 groups of ~600 rows at
     d 1024, F 1536 (256 x 128 tiles, two blocks a CU); and the switch
     workload's groups of at most 256 rows at N 4096, K 1024 (128 x 256 tiles)
     and at N 1024, K 4096 (64-wide K stages in a 4-stage ring).  Guards the
