@@ -7,7 +7,9 @@ synthetic inputs already resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload default]
 
-Steps are timed as K replays of one HIP graph holding the whole pass.  Per-call
+Steps are timed as one replay of a HIP graph holding the K timed passes back
+to back (``ms_per_step_graph_each`` gives K replays of a one-step graph, which
+adds the runtime's per-graph launch gap to every step).  Per-call
 durations come from HIP events on the stream the kernels run on (torch's
 current stream, which every call is given) around K replays of a graph holding
 R back-to-back launches of that one call, with the queue kept full so the
@@ -156,25 +158,44 @@ def main():
     K = args.steps
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    # Whole steps: one step captured as a HIP graph and replayed K times.  A
-    # sleep kernel keeps the GPU busy while the host queues the replays, so the
-    # events see back-to-back steps, not host launch latency.
+    # Whole steps: the K timed steps captured back to back in one HIP graph
+    # (as the layers of a model would be) and replayed once between two
+    # events, after one untimed replay.  A sleep kernel keeps the GPU busy
+    # while the host queues the replay, so the events see the GPU only.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step()
-    for _ in range(args.warmup):
-        graph.replay()
+        for _ in range(K):
+            step()
+    graph.replay()
     torch.cuda.synchronize()
     start, stop = ev(), ev()
     wall0 = time.perf_counter()
-    torch.cuda._sleep(int(2.4e9 * 200e-6 * K))
+    torch.cuda._sleep(int(2.4e9 * 100e-6))
     start.record()
-    for _ in range(K):
-        graph.replay()
+    graph.replay()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / K
+    del graph
+
+    # The same K steps as K replays of a one-step graph: each replay adds the
+    # runtime's per-graph launch gap (reported alongside, not as the value).
+    graph1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph1):
+        step()
+    for _ in range(args.warmup):
+        graph1.replay()
+    torch.cuda.synchronize()
+    a1, b1 = ev(), ev()
+    torch.cuda._sleep(int(2.4e9 * 200e-6 * K))
+    a1.record()
+    for _ in range(K):
+        graph1.replay()
+    b1.record()
+    torch.cuda.synchronize()
+    ms_step_graph_each = a1.elapsed_time(b1) / K
+    del graph1
 
     # Per call: each call captured R times back to back in a graph of its own
     # and replayed K times between two events (queue pre-filled the same way),
@@ -258,6 +279,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_step_calls": ms_step_eager,     # sum of the per-call times
+        "ms_per_step_graph_each": ms_step_graph_each,   # K replays of a one-step graph
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
