@@ -125,8 +125,8 @@ def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this layer has no multi-GPU path (see DESIGN.md, "
-              "sharding); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this layer has no multi-GPU path (expert "
+              "parallelism is designed, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
