@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "lds_ring.h"
 
 namespace moe {
 
@@ -680,6 +681,129 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
   if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
 }
 
+// The partials and the finish in one kernel, for E = EP: a block
+// takes RW = 16 NW tokens against all 3E split-weight rows, and wave w owns
+// tokens 16 w .. 16 w + 15 over every column, so after the K loop each lane
+// holds the hi, mid and lo partials of the same experts.  The K loop runs
+// 32-wide stages through an NS-stage LDS ring with the grouped GEMM's MFMA in
+// the same K order, so the fp32 partials are the ones the GEMM writes; the
+// fp64 logits ((hi + mid) + lo, the finish kernel's order) go through LDS to
+// the same per-token epilogue, NXE lanes a token.  The results are those of
+// the split GEMM and the finish kernel, without the 3E-column partials buffer.
+template <int EP, int NW, int NS>
+__global__ __launch_bounds__(64 * NW) void router_mfma_kernel(
+    const bf16_t* __restrict__ x, int64_t T, int d, const bf16_t* __restrict__ Ws, int k,
+    const float* __restrict__ bg, const float* __restrict__ bsel, float* __restrict__ logits,
+    float* __restrict__ lse_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ count, int32_t* __restrict__ list, const float* __restrict__ noise,
+    double sigma) {
+  constexpr int E = EP;
+  constexpr int RW = 16 * NW;          // tokens a block
+  constexpr int NR = RW + 3 * E;       // stage rows: the tokens, then hi, mid, lo weight rows
+  constexpr int SLAB = NR * 64;        // 32 bf16 of K a row
+  constexpr int LPW = NR / (16 * NW);  // 1 KB load instructions a wave per stage (16 rows each)
+  constexpr int TN = 3 * E / 16;       // MFMA column tiles a wave
+  static_assert(NR % (16 * NW) == 0, "stage rows split evenly over the waves");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  __shared__ __attribute__((aligned(1024))) char st0[SLAB];
+  __shared__ __attribute__((aligned(1024))) char st1[SLAB];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? SLAB : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? SLAB : 16];
+  __shared__ double s_h[RW * E];
+  char* const stages[4] = {st0, st1, st2, st3};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * RW;
+
+  // load slots: instruction j = wave + NW i fills rows 16 j .. 16 j + 15, lane l
+  // row 16 j + l / 4 at physical chunk l % 4 (token rows past T reload row T - 1)
+  const bf16_t* src[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = 16 * (wave + NW * i) + lane / 4;
+    const int chunk = (lane % 4) ^ swz<1>(row);
+    if (row < RW) {
+      const int64_t t = t0 + row < T ? t0 + row : T - 1;
+      src[i] = x + t * d + chunk * 8;
+    } else {
+      src[i] = Ws + (int64_t)(row - RW) * d + chunk * 8;
+    }
+  }
+  const int nk = d / 32;
+  auto issue = [&](int kt, int stage) {
+    const int kk = (kt < nk ? kt : nk - 1) * 32;  // past the end: harmless reload
+    char* base = stages[stage];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kk),
+                                       (lds_ptr_t)(base + 16 * (wave + NW * i) * 64), 16, 0, 0);
+  };
+  // operand reads: lane (fr, fc) reads row fr of a 16-row tile at logical chunk fc
+  const int fr = lane & 15, fc = lane >> 4;
+  int a_rd, b_rd[TN];
+  {
+    const int R = wave * 16 + fr;
+    a_rd = R * 64 + ((fc ^ swz<1>(R)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int R = RW + j * 16 + fr;
+    b_rd[j] = R * 64 + ((fc ^ swz<1>(R)) << 4);
+  }
+  f32x4_t acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  auto step = [&](int kt, int stage) {
+    wait_vmcnt<(NS - 2) * LPW>();  // this wave's loads of stage kt have landed
+    slab_barrier();                 // ... and every other wave's
+    issue(kt + NS - 1, (stage + NS - 1) % NS);
+    const char* base = stages[stage];
+    const bf16x8_t a = *(const bf16x8_t*)(base + a_rd);
+    bf16x8_t b[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[j]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a, acc[j], 0, 0, 0);
+  };
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) step(kt + s, s);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (kt + s < nk) step(kt + s, s);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // lane (fr, fc) holds token 16 wave + fr at columns 16 j + 4 fc + r: hi for
+  // column e, mid for E + e, lo for 2E + e (the + 0 is the GEMM's bias add)
+#pragma unroll
+  for (int j = 0; j < E / 16; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double h = (double)(acc[j][r] + 0.f) + (double)(acc[E / 16 + j][r] + 0.f) +
+                       (double)(acc[2 * E / 16 + j][r] + 0.f);
+      s_h[(wave * 16 + fr) * E + j * 16 + fc * 4 + r] = h;
+    }
+  __syncthreads();
+  constexpr int NXE = 16, TE = E / NXE, TPP = 64 * NW / NXE;  // lanes a token, experts a lane, tokens a pass
+  const int eg = tid % NXE;
+#pragma unroll 1
+  for (int p = 0; p < RW / TPP; ++p) {
+    const int tl = p * TPP + tid / NXE;
+    const int64_t t = t0 + tl;
+    double a[TE];
+#pragma unroll
+    for (int j = 0; j < TE; ++j) a[j] = s_h[tl * E + eg + NXE * j];
+    const bool near = token_epilogue<TE, NXE>(a, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
+                                              topk_idx, topk_gate, noise, sigma, kRefineRel);
+    if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
+  }
+}
+
 // Exact fp64 recomputation of the listed tokens, one token per block at a time.
 // Exact recomputation of the listed tokens, in two kernels.
 //  * dots: the work items (listed token i, slice of 16 experts) are spread over
@@ -785,16 +909,33 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   const int64_t nb = (n + 255) / 256;
   hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, Wg,
                      E, d, Ws, count);
-  GemmArgs g{};
-  g.A = x; g.group_offset = nullptr; g.G = 1; g.dense_M = T; g.max_rows = T;
-  g.B = Ws; g.N = 3 * E; g.K = d; g.S = 1; g.Kseg = d; g.bias = nullptr; g.C = part;
-  g.act = -1; g.sq_part = nullptr; g.out_f32 = true;
-  hipError_t e = launch_gemm_bf16(g, st);
-  if (e != hipSuccess) return e;
-  constexpr int NXE = (EP >= 256) ? 32 : 16;
-  const int64_t tpb = 256 / NXE;
-  hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
-                     part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma);
+  bool fused = false;
+  if constexpr (EP == 64) {
+    // partials and finish in one kernel where it measured faster: 64 experts
+    // and 256 or more blocks of 64 tokens (switch layer, T 16384, d 1024:
+    // routing pass 48.7 -> 46.7 us).  With fewer tokens (two-wave blocks:
+    // 64 experts at T 8192, d 2048, 60.6 -> 69.5 us) or 128 experts (every
+    // block re-reads 3 MB of split weights: 264 -> 324 us at T 32768, d 4096)
+    // the GEMM and the finish kernel stay ahead.
+    if (E == EP && T >= 64 * 256) {
+      hipLaunchKernelGGL((router_mfma_kernel<EP, 4, 4>), dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st,
+                         (const bf16_t*)x, T, d, Ws, k, bg, bsel, logits, lse, idx, gate, count, list,
+                         noise, sigma);
+      fused = true;
+    }
+  }
+  if (!fused) {
+    GemmArgs g{};
+    g.A = x; g.group_offset = nullptr; g.G = 1; g.dense_M = T; g.max_rows = T;
+    g.B = Ws; g.N = 3 * E; g.K = d; g.S = 1; g.Kseg = d; g.bias = nullptr; g.C = part;
+    g.act = -1; g.sq_part = nullptr; g.out_f32 = true;
+    hipError_t e = launch_gemm_bf16(g, st);
+    if (e != hipSuccess) return e;
+    constexpr int NXE = (EP >= 256) ? 32 : 16;
+    const int64_t tpb = 256 / NXE;
+    hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
+                       part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma);
+  }
   // the listed tokens' exact logits go into the consumed partials buffer
   // (T E doubles <= T 3E floats)
   double* h = (double*)part;

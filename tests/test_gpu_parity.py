@@ -447,14 +447,17 @@ def test_graph_replay_matches_eager():
                                r.view(torch.int16) if r.dtype == torch.bfloat16 else r), (rep, n)
 
 
-@pytest.mark.parametrize("E,d,k", [(128, 512, 8), (64, 1024, 6), (40, 2048, 2)])
-def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k):
+@pytest.mark.parametrize("E,d,k,T", [(128, 512, 8, 4096), (64, 1024, 6, 4096), (40, 2048, 2, 4096),
+                                     (64, 1024, 4, 16411)])
+def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k, T):
     """bf16 x with a large W_g uses the split-W_g MFMA router; tokens near a tie
     are recomputed in fp64, so the selection equals the float64 oracle's except
     where the float64 gap itself is at rounding level.  Planted: an exact
     duplicate row (exact ties: lower index wins), a row one fp32 ulp away
-    (gaps ~1e-7) and a row 1e-6 away."""
-    w = synth.LARGE_CREDIT.with_(T=4096, d=d, F=32, E=E, k=k)
+    (gaps ~1e-7) and a row 1e-6 away.  E 64 at T 16411 takes the fused
+    partials-and-finish kernel (blocks of 64 tokens, the last one partial);
+    the others the split GEMM and the finish kernel."""
+    w = synth.LARGE_CREDIT.with_(T=T, d=d, F=32, E=E, k=k)
     inp = synth.draw(w)
     Wg = inp.W_g.copy()
     Wg[5] = Wg[3]
