@@ -114,6 +114,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const bool books = c == nchunks;  // uniform: the bookkeeping block
   const int64_t t = c * kDispatchChunk + lane;
   const int64_t grp = books ? nunits : c * kDispatchChunk / unit_tokens;  // units before the chunk
+  const int ngroups = unit_tokens == kStatsSub ? (nunits + kStatsSubs - 1) / kStatsSubs : nunits;  // statistics groups
 
   for (int e = tid; e < E; e += 256) {
     s_base[e] = 0;
@@ -139,11 +140,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int v0[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v0[u] = (q < Q && q + u * Q < nunits) ? group[(int64_t)(q + u * Q) * E + e] : 0;
-    if (books && f != nullptr) {
-      const bool sub = unit_tokens == kStatsSub;
-      const int ngroups = sub ? (nunits + kStatsSubs - 1) / kStatsSubs : nunits;
-      stats_finish_sums(part, ngroups, E, s_red, s_z, sub ? nunits : 0);
-    }
+    if (books && f != nullptr) stats_finish_sums(part, ngroups, E, s_red, s_z, unit_tokens == kStatsSub ? nunits : 0);
     if (q < Q) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     for (int e = tid; e <= E; e += 256) offset[e] = s_off[e];
     // statistics: the sums were taken above (group values stored for units of
     // 256, summed from the 16-token sub-partials otherwise: the same order)
-    if (f != nullptr) stats_finish_write(s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
+    if (f != nullptr) stats_finish_write(s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z, ngroups);
     return;
   }
 

@@ -100,14 +100,37 @@ __device__ __forceinline__ double stats_group_value(const double* __restrict__ p
 // order (left in s_red[q E + e]); the lse^2 column by all 256 threads
 // (groups tid, tid + 256, ...) and a pairwise tree (left in s_z[0]).
 // s_red, s_z: 256 doubles each.
+// Every partial is a sum of non-negative terms, so adding a +0 leaves it
+// unchanged: tree levels whose upper half lies past nparts are skipped, and
+// with nparts <= 64 the rest runs in wave 0 with shuffles pairing the same
+// entries (lane i adds lane i + w), without LDS or barriers.
 __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ part, int nparts, int E,
                                                   double* s_red, double* s_z, int64_t nsub = 0) {
   const int tid = threadIdx.x;
   const int C = E + 1;
   const int Q = 256 / E;
-  {
-    const int e = tid % E, q = tid / E;
-    double s = 0.0;
+  double s = 0.0, z = 0.0;
+  const int e = tid % E, q = tid / E;
+  if (nsub > 0 && nparts <= Q) {
+    // at most one group a thread in either sum: both groups' sub-partials
+    // are loaded before either is added up
+    const bool has_e = q < nparts, has_z = tid < nparts;
+    const int64_t re = (int64_t)q * kStatsSubs, rz = (int64_t)tid * kStatsSubs;
+    double ve[kStatsSubs], vz[kStatsSubs];
+#pragma unroll
+    for (int i = 0; i < kStatsSubs; ++i) {
+      ve[i] = (has_e && re + i < nsub) ? part[(re + i) * C + e] : 0.0;
+      vz[i] = (has_z && rz + i < nsub) ? part[(rz + i) * C + E] : 0.0;
+    }
+    double ge = 0.0, gz = 0.0;
+#pragma unroll
+    for (int i = 0; i < kStatsSubs; ++i) {
+      ge += ve[i];
+      gz += vz[i];
+    }
+    if (has_e) s += ge;
+    if (has_z) z += gz;
+  } else {
     if (q < Q) {
       int b = q;
       for (; b + 3 * Q < nparts; b += 4 * Q) {
@@ -122,41 +145,63 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
       }
       for (; b < nparts; b += Q) s += stats_group_value(part, b, e, C, nsub);
     }
-    double z = 0.0;
     for (int b = tid; b < nparts; b += 256) z += stats_group_value(part, b, E, C, nsub);
-    s_red[tid] = s;
-    s_z[tid] = z;
   }
+  s_red[tid] = s;
+  if (nparts <= 64) {
+    if (tid < 64) {
+#pragma unroll
+      for (int w = 32; w > 0; w >>= 1) {
+        const double o = __shfl_down(z, w, 64);
+        if (w < nparts) z += o;
+      }
+      if (tid == 0) s_z[0] = z;
+    }
+    __syncthreads();
+    return;
+  }
+  s_z[tid] = z;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) s_z[tid] += s_z[tid + w];
-    __syncthreads();
+    if (w < nparts) {  // uniform
+      if (tid < w) s_z[tid] += s_z[tid + w];
+      __syncthreads();
+    }
   }
 }
 
 // Second half: f, P and the losses from those sums and the pre-capacity counts.
+// Thread rows q >= nparts summed no group (+0), so the expert sums stop there;
+// with E <= 64 the E products are summed in order in wave 0 from its lanes.
 __device__ __forceinline__ void stats_finish_write(const int32_t* count, int64_t T, int E, int k,
                                                    float alpha, float beta, float* __restrict__ f,
                                                    float* __restrict__ Pm, float* __restrict__ losses,
-                                                   double* s_red, double* s_z) {
+                                                   double* s_red, double* s_z, int nparts) {
   const int tid = threadIdx.x;
   const int Q = 256 / E;
+  const int qn = nparts < Q ? nparts : Q;
   double fp_e = 0.0;
   if (tid < E) {
     double s = 0.0;
-    for (int q = 0; q < Q; ++q) s += s_red[q * E + tid];
+    for (int q = 0; q < qn; ++q) s += s_red[q * E + tid];
     const double pe = s / (double)T;
     const double fe = (double)count[tid] / ((double)k * (double)T);
     Pm[tid] = (float)pe;
     f[tid] = (float)fe;
     fp_e = fe * pe;
   }
-  __syncthreads();
-  if (tid < E) s_red[tid] = fp_e;
-  __syncthreads();
+  double fp = 0.0;
+  if (E <= 64) {
+    if (tid >= 64) return;  // wave 0 holds every product
+    for (int ee = 0; ee < E; ++ee) fp += __shfl(fp_e, ee, 64);
+  } else {
+    __syncthreads();
+    if (tid < E) s_red[tid] = fp_e;
+    __syncthreads();
+    if (tid == 0)
+      for (int ee = 0; ee < E; ++ee) fp += s_red[ee];
+  }
   if (tid == 0) {
-    double fp = 0.0;
-    for (int ee = 0; ee < E; ++ee) fp += s_red[ee];
     const double la = (double)alpha * (double)E * fp;
     const double lz = (double)beta * s_z[0] / (double)T;
     losses[0] = (float)la;
@@ -171,7 +216,7 @@ __device__ __forceinline__ void stats_finish(const double* __restrict__ part, in
                                              float* __restrict__ Pm, float* __restrict__ losses,
                                              double* s_red, double* s_z, int64_t nsub = 0) {
   stats_finish_sums(part, nparts, E, s_red, s_z, nsub);
-  stats_finish_write(count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
+  stats_finish_write(count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z, nparts);
 }
 
 }  // namespace moe
