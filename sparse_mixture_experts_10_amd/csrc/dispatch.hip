@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __r
 
 // One block per chunk of 64 tokens (wave 0 ranks, all four waves copy rows),
 // plus one bookkeeping block (blockIdx.x == nchunks) that writes the counts and
-// offsets and, in the fused routing pass, the statistics.
+// offsets and, in the fused routing pass, a statistics block (nchunks + 1)
+// that takes the totals again and finishes the statistics, so the counts do
+// not wait behind the statistics' loads and sums.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int nunits, int unit_tokens,
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int wave = tid >> 6;
   const int64_t c = blockIdx.x;
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
-  const bool books = c == nchunks;  // uniform: the bookkeeping block
+  const bool books = c >= nchunks;       // uniform: a bookkeeping block (counts / statistics)
+  const bool stat_blk = c == nchunks + 1;  // the statistics block
   const int64_t t = c * kDispatchChunk + lane;
   const int64_t grp = books ? nunits : c * kDispatchChunk / unit_tokens;  // units before the chunk
   const int ngroups = unit_tokens == kStatsSub ? (nunits + kStatsSubs - 1) / kStatsSubs : nunits;  // statistics groups
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int v0[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v0[u] = (q < Q && q + u * Q < nunits) ? group[(int64_t)(q + u * Q) * E + e] : 0;
-    if (books && f != nullptr) stats_finish_sums(part, ngroups, E, s_red, s_z, unit_tokens == kStatsSub ? nunits : 0);
+    if (stat_blk) stats_finish_sums(part, ngroups, E, s_red, s_z, unit_tokens == kStatsSub ? nunits : 0);
     if (q < Q) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -174,6 +177,12 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     }
   }
   __syncthreads();
+  if (stat_blk) {
+    // statistics: the sums were taken above (group values stored for units of
+    // 256, summed from the 16-token sub-partials otherwise: the same order)
+    stats_finish_write(s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z, ngroups);
+    return;
+  }
   int kept = 0;
   if (tid < E) {
     const int tot = s_cnt[tid];
@@ -202,9 +211,6 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   if (books) {
     for (int e = tid; e < E; e += 256) count[e] = s_cnt[e];
     for (int e = tid; e <= E; e += 256) offset[e] = s_off[e];
-    // statistics: the sums were taken above (group values stored for units of
-    // 256, summed from the 16-token sub-partials otherwise: the same order)
-    if (f != nullptr) stats_finish_write(s_cnt, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z, ngroups);
     return;
   }
 
@@ -278,7 +284,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
                        ws.part);
   }
   const int64_t vpr = (int64_t)d * elem_bytes / 16;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)(nchunks + 1)), dim3(256), 0, st, idx, T, k, E,
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)(nchunks + (stats ? 2 : 1))), dim3(256), 0, st, idx, T, k, E,
                      capacity, ws.hist, ws.group, (int)nunits, unit, count, offset, slot, row, row_token,
                      (const vec16*)x, vpr, (vec16*)x_disp, ws.part, stats ? stats->alpha : 0.f,
                      stats ? stats->beta : 0.f, stats ? stats->f : nullptr, stats ? stats->P : nullptr,
