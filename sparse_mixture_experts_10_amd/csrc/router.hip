@@ -21,12 +21,15 @@
 //  * K-split (router_ksplit_kernel, used when W_g fits in LDS): 16 lanes per
 //    token each sum a 1/16 slice of d for every expert against W_g held whole
 //    in LDS, then a recursive-halving reduce-scatter leaves lane eg with the
-//    sums of its experts.  Many more tokens in flight for small E.
+//    sums of its experts.  Many more tokens in flight for small E.  Small
+//    batches give each of those 16 slices two lanes, one per half of the
+//    experts (same products, same order, same bits), for twice the waves.
 
 #include <type_traits>
 
 #include "common.h"
 #include "internal.h"
+#include "gemm_tiles.h"
 #include "lds_ring.h"
 
 namespace moe {
@@ -416,8 +419,8 @@ __device__ __forceinline__ void rs_halve(const double (&v)[N], double (&w)[N / 2
   }
 }
 
-constexpr int KS_LPT = 16;    // lanes per token
-constexpr int KS_TPB = 16;    // tokens per block (256 threads)
+constexpr int KS_LPT = 16;    // column slices per token (a slice: one lane, or two splitting the experts)
+constexpr int KS_TPB = 16;    // tokens per block (256 threads, 512 with split experts)
 static_assert(KS_TPB == kStatsSub, "a counting router block is one statistics sub-block");
 constexpr int KS_XV = 16;     // x vectors per lane: d <= 16 * 16 * 8 (bf16) or 16 * 16 * 4 (fp32)
 constexpr int KS_FB = 4;      // W_g float4 loads a thread has in flight during the LDS fill
@@ -442,8 +445,15 @@ static size_t ks_lds_bytes(int E, int d, bool xbf16) {
   return (size_t)ks_expert_rows(E) * ks_row_float4(d, xbf16) * sizeof(float4);
 }
 
-template <int EP, bool XBF16>
-__global__ __launch_bounds__(256) void router_ksplit_kernel(
+// SPLIT: two lanes per column slice, lane 16 h + s of a token's 32 taking
+// experts h EP / 2 .. (h + 1) EP / 2 - 1 of slice s (512 threads a block).  For
+// one wave a SIMD the fp64 FMA chains stall on their latency (measured on
+// MI355X: 9.7 cycles per wave instruction with one wave, 5.8 with two, 4.8
+// with eight); after the K loop the two halves swap their sums, so every lane
+// holds what the unsplit lane holds and the reduction and epilogue are the
+// same code.
+template <int EP, bool XBF16, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
     const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
@@ -455,15 +465,20 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
   __shared__ float tap_p[KS_TPB][EP];
   __shared__ float tap_lse[KS_TPB];
   __shared__ int tap_hist[EP];
+  // split: the reduced sums of each token's 16 slices, handed to waves 0-3
+  __shared__ double s_r[SPLIT ? KS_TPB * KS_LPT : 1][(EP >= 16) ? EP / 16 : 1];
   constexpr int XW = XBF16 ? 8 : 4;   // elements per 16-byte x vector
   constexpr int CH = KS_LPT * XW;     // columns per chunk
   constexpr int CH4 = CH / 4;         // float4 per chunk
   // chunks a 64 KB W_g copy of EP rows can hold: the most x vectors a lane needs
   constexpr int XV = (16384 / (EP * CH)) < KS_XV ? 16384 / (EP * CH) : KS_XV;
   static_assert(XV >= 1, "W_g rows do not fit the LDS budget");
+  constexpr int NT = KS_TPB * KS_LPT * (SPLIT ? 2 : 1);  // threads
+  constexpr int EPH = SPLIT ? EP / 2 : EP;                 // experts a lane sums
   const int tid = threadIdx.x;
   const int lane = tid & (KS_LPT - 1);
-  const int64_t t = (int64_t)blockIdx.x * KS_TPB + tid / KS_LPT;
+  const int half = SPLIT ? (tid >> 4) & 1 : 0;
+  const int64_t t = (int64_t)blockIdx.x * KS_TPB + tid / (NT / KS_TPB);
   const int row4 = ks_row_float4(d, XBF16);
 
   // this lane's slice of the token row, loaded before the W_g fill so both
@@ -486,11 +501,11 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
   // W_g -> LDS, EP rows (rows past E and columns past d are zero): KS_FB loads
   // in flight per thread, then their stores
   const int nv4 = EP * row4;
-  for (int v0 = 0; v0 < nv4; v0 += 256 * KS_FB) {
+  for (int v0 = 0; v0 < nv4; v0 += NT * KS_FB) {
     float4 q[KS_FB];
 #pragma unroll
     for (int i = 0; i < KS_FB; ++i) {
-      const int v = v0 + tid + 256 * i;
+      const int v = v0 + tid + NT * i;
       q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (v < nv4) {
         const int e = v / row4, r = v - e * row4;
@@ -501,16 +516,16 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     }
 #pragma unroll
     for (int i = 0; i < KS_FB; ++i) {
-      const int v = v0 + tid + 256 * i;
+      const int v = v0 + tid + NT * i;
       if (v < nv4) wsm[v] = q[i];
     }
   }
   __syncthreads();
 
   // no expert or column guards: the padding is zero (nit is uniform)
-  double acc[EP];
+  double acc[EPH];
 #pragma unroll
-  for (int e = 0; e < EP; ++e) acc[e] = 0.0;
+  for (int e = 0; e < EPH; ++e) acc[e] = 0.0;
 #pragma unroll
   for (int it = 0; it < XV; ++it) {
     if (it < nit) {
@@ -527,28 +542,43 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
       // all of this chunk's W_g quarters first, then one column at a time
       // across the experts: EP independent fp64 chains, no load-use stall
       // per expert
-      const float4* wl = wsm + it * CH4 + lane;
+      const float4* wl = wsm + it * CH4 + lane + half * EPH * row4;
       constexpr int NQ = XW / 4;
+      constexpr int GE = EPH < 8 ? EPH : 8;  // experts whose quarters are read together
 #pragma unroll
-      for (int e0 = 0; e0 < EP; e0 += 8) {
-        float4 w[8][NQ];
+      for (int e0 = 0; e0 < EPH; e0 += GE) {
+        float4 w[GE][NQ];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < GE; ++e)
 #pragma unroll
           for (int h = 0; h < NQ; ++h) w[e][h] = wl[(e0 + e) * row4 + 16 * h];
 #pragma unroll
         for (int h = 0; h < NQ; ++h) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 0], (double)w[e][h].x, acc[e0 + e]);
+          for (int e = 0; e < GE; ++e) acc[e0 + e] = fma(f[4 * h + 0], (double)w[e][h].x, acc[e0 + e]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 1], (double)w[e][h].y, acc[e0 + e]);
+          for (int e = 0; e < GE; ++e) acc[e0 + e] = fma(f[4 * h + 1], (double)w[e][h].y, acc[e0 + e]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 2], (double)w[e][h].z, acc[e0 + e]);
+          for (int e = 0; e < GE; ++e) acc[e0 + e] = fma(f[4 * h + 2], (double)w[e][h].z, acc[e0 + e]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e0 + e] = fma(f[4 * h + 3], (double)w[e][h].w, acc[e0 + e]);
+          for (int e = 0; e < GE; ++e) acc[e0 + e] = fma(f[4 * h + 3], (double)w[e][h].w, acc[e0 + e]);
         }
       }
     }
+  }
+
+  // split halves: swap sums so both lanes of a slice hold all EP experts
+  double all[EP];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int j = 0; j < EPH; ++j) {
+      const double other = xor_lane_d<16>(acc[j]);
+      all[j] = half ? other : acc[j];
+      all[EPH + j] = half ? acc[j] : other;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EP; ++e) all[e] = acc[e];
   }
 
   // reduce-scatter over the 16 lanes: lane l ends with experts l + 16 j
@@ -558,22 +588,42 @@ __global__ __launch_bounds__(256) void router_ksplit_kernel(
     double a4[4], a2[2];
     double full[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) full[e] = acc[e] + xor_lane_d<8>(acc[e]);
+    for (int e = 0; e < 8; ++e) full[e] = all[e] + xor_lane_d<8>(all[e]);
     rs_halve<8, 4>(full, a4, lane);
     rs_halve<4, 2>(a4, a2, lane);
     rs_halve<2, 1>(a2, r, lane);
   } else {
     double b8[EP / 2], b4[EP / 4], b2[EP / 8];
-    rs_halve<EP, 8>(acc, b8, lane);
+    rs_halve<EP, 8>(all, b8, lane);
     rs_halve<EP / 2, 4>(b8, b4, lane);
     rs_halve<EP / 4, 2>(b4, b2, lane);
     rs_halve<EP / 8, 1>(b2, r, lane);
   }
   // for EP = 8, lanes 8..15 duplicate lanes 0..7; their expert ids lane >= 8 >= E are void
-  const int tl = tid / KS_LPT;
-  RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
-  token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                             noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+  if constexpr (SPLIT) {
+    // the first half's sums go through LDS to waves 0-3 (16 lanes a token,
+    // as unsplit), which run the epilogue; waves 4-7 skip it
+    if (half == 0) {
+#pragma unroll
+      for (int j = 0; j < TE; ++j) s_r[(tid >> 5) * KS_LPT + lane][j] = r[j];
+    }
+    __syncthreads();
+    if (tid < KS_TPB * KS_LPT) {  // uniform per wave
+      double rr[TE];
+#pragma unroll
+      for (int j = 0; j < TE; ++j) rr[j] = s_r[tid][j];
+      const int tl = tid / KS_LPT;
+      const int64_t tt = (int64_t)blockIdx.x * KS_TPB + tl;
+      RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
+      token_epilogue<TE, KS_LPT>(rr, lane, tt, tt < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
+                                 noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+    }
+  } else {
+    const int tl = tid / KS_LPT;
+    RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
+    token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
+                               noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+  }
   if (hist16 == nullptr) return;  // uniform
   __syncthreads();
   // per expert: choices among the block's tokens and the softmax mass summed
@@ -608,14 +658,22 @@ static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int
                                        float* logits, float* lse, int32_t* idx, float* gate,
                                        const float* noise, double sigma, int32_t* hist16,
                                        double* p16, hipStream_t st) {
-  const dim3 grid((unsigned)((T + KS_TPB - 1) / KS_TPB));
+  const int64_t blocks = (T + KS_TPB - 1) / KS_TPB;
+  const dim3 grid((unsigned)blocks);
   const size_t lds = ks_lds_bytes(E, d, xbf16);
-  if (xbf16)
-    hipLaunchKernelGGL((router_ksplit_kernel<EP, true>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16);
-  else
-    hipLaunchKernelGGL((router_ksplit_kernel<EP, false>), grid, dim3(256), lds, st, x, T, d, Wg, bg,
-                       bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16);
+  // split experts when the batch gives at most one block (four waves) a CU
+  const bool split = blocks <= kCus;
+#define MOE_KS_LAUNCH(XB, SP)                                                                              \
+  hipLaunchKernelGGL((router_ksplit_kernel<EP, XB, SP>), grid, dim3(SP ? 512 : 256), lds, st, x, T, d, Wg, bg, \
+                     bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16)
+  if (xbf16) {
+    if (split) MOE_KS_LAUNCH(true, true);
+    else MOE_KS_LAUNCH(true, false);
+  } else {
+    if (split) MOE_KS_LAUNCH(false, true);
+    else MOE_KS_LAUNCH(false, false);
+  }
+#undef MOE_KS_LAUNCH
   return hipGetLastError();
 }
 

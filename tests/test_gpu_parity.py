@@ -489,3 +489,36 @@ def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k, T):
     P, lse_ref = oracle.softmax_lse(h)
     assert close(lse.cpu().numpy().astype(np.float64), lse_ref, 1e-5).all()
     assert close(g.cpu().numpy().astype(np.float64), oracle.gates(P, got.astype(np.int64)), 1e-5).all()
+
+
+@pytest.mark.parametrize("E,d,k,dtype", [(8, 512, 2, "bf16"), (32, 256, 4, "bf16"), (7, 40, 3, "f32")])
+def test_router_ksplit_results_do_not_depend_on_the_batch(E, d, k, dtype):
+    """The K-split router gives each column slice of a token two lanes (one per
+    half of the experts) when the batch fills at most one block per CU, and one
+    lane otherwise; both sum the same products in the same order.  The first
+    4096 tokens routed alone and inside a batch of 9000 give the same bits, and
+    both match the float64 oracle."""
+    w = synth.DEFAULT.with_(T=9000, d=d, F=32, E=E, k=k, dtype=dtype)
+    inp = synth.draw(w)
+    say(f"[gpu] k-split router batch invariance E={E} d={d} k={k} dtype={dtype}")
+    from synth.device import to_torch
+    t = to_torch(inp)
+    outs = []
+    for T in (4096, 9000):
+        lg = torch.empty(T, E, device="cuda"); lse = torch.empty(T, device="cuda")
+        idx = torch.empty(T, k, dtype=torch.int32, device="cuda"); g = torch.empty(T, k, device="cuda")
+        assert api.moe_workspace_bytes(api.OP_ROUTER, T=T, d=d, E=E) == 0   # the K-split path
+        api.moe_router_topk(t["x"][:T], t["W_g"], t["b_g"], t["b_sel"], k, lg, lse, idx, g)
+        torch.cuda.synchronize()
+        outs.append((lg, lse, idx, g))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b[:4096])
+    lg, lse, idx, g = outs[1]
+    h = oracle.router_logits(synth.widen(inp.x, dtype), inp.W_g, inp.b_g)
+    ref = oracle.topk(h, k, inp.b_sel)
+    gap = oracle.near_tie_gap(h, k, inp.b_sel)
+    got = idx.cpu().numpy()
+    for tt in np.nonzero((got != ref).any(axis=1))[0]:
+        assert gap[tt] < 1e-12, (tt, got[tt], ref[tt], gap[tt])
+    close = lambda a, b, tol: np.abs(a - b) <= tol * np.maximum(1, np.abs(b))
+    assert close(lg.cpu().numpy().astype(np.float64), h, 1e-5).all()
