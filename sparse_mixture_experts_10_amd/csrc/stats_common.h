@@ -87,9 +87,11 @@ __device__ __forceinline__ double stats_group_value(const double* __restrict__ p
   double v[kStatsSubs];
 #pragma unroll
   for (int i = 0; i < kStatsSubs; ++i) v[i] = (r0 + i < nsub) ? part[(r0 + i) * C + col] : 0.0;
-  double g = 0.0;
+  // 0.0 + v[0] is v[0] (the partials are non-negative): starting from v[0]
+  // also keeps the compiler from waiting on that load right where it is issued
+  double g = v[0];
 #pragma unroll
-  for (int i = 0; i < kStatsSubs; ++i) g += v[i];
+  for (int i = 1; i < kStatsSubs; ++i) g += v[i];
   return g;
 }
 
@@ -122,9 +124,9 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
       ve[i] = (has_e && re + i < nsub) ? part[(re + i) * C + e] : 0.0;
       vz[i] = (has_z && rz + i < nsub) ? part[(rz + i) * C + E] : 0.0;
     }
-    double ge = 0.0, gz = 0.0;
+    double ge = ve[0], gz = vz[0];  // = 0.0 + v[0]: the partials are non-negative
 #pragma unroll
-    for (int i = 0; i < kStatsSubs; ++i) {
+    for (int i = 1; i < kStatsSubs; ++i) {
       ge += ve[i];
       gz += vz[i];
     }
