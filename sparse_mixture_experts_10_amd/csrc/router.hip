@@ -135,6 +135,34 @@ struct RouterTap {
   int* hist;    // [E], shared by the block
 };
 
+// Router bias b_g and selection bias b_sel of the experts lane eg holds in the
+// epilogue below (0 where absent; rows past E read expert E - 1, unused).  All
+// loads are issued together; a kernel may take them before its main loop so
+// the epilogue does not wait on them.
+template <int TE>
+struct RouterBias {
+  float g[TE], s[TE];
+};
+
+// Zeros read in place of an absent bias, so the loads need no branch (a
+// load under a branch whose result is converted gets its wait inside it).
+__device__ float kNoBias[kMaxExperts];
+
+template <int TE, int NXE>
+__device__ __forceinline__ RouterBias<TE> load_router_bias(const float* __restrict__ bg,
+                                                           const float* __restrict__ bsel, int eg, int E) {
+  const float* pg = bg != nullptr ? bg : kNoBias;
+  const float* ps = bsel != nullptr ? bsel : kNoBias;
+  RouterBias<TE> b;
+#pragma unroll
+  for (int j = 0; j < TE; ++j) {
+    const int e = eg + NXE * j < E ? eg + NXE * j : E - 1;
+    b.g[j] = pg[e];
+    b.s[j] = ps[e];
+  }
+  return b;
+}
+
 // Per-token epilogue.  The NXE lanes of a token hold its fp64 dot products
 // (router bias not yet added): lane eg holds experts e = eg + NXE j, j < TE.
 // With noise != nullptr the logits are h + sigma * noise[t, e] (noisy top-k,
@@ -154,18 +182,30 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
                                                int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_gate,
                                                const float* __restrict__ noise, double sigma,
-                                               double flag_rel = 0.0, RouterTap* tap = nullptr) {
+                                               double flag_rel = 0.0, RouterTap* tap = nullptr,
+                                               const RouterBias<TE>* pre = nullptr) {
   const double NEG = -__builtin_huge_val();
+  // every bias and noise load is issued before the first is used (a load
+  // under a per-expert branch gets a wait of its own)
+  const RouterBias<TE> rb = pre != nullptr ? *pre : load_router_bias<TE, NXE>(bg, bsel, eg, E);
+  float nz[TE];
+#pragma unroll
+  for (int j = 0; j < TE; ++j) nz[j] = 0.f;
+  if (noise != nullptr) {  // uniform
+    const float* pn = live ? noise + t * E : kNoBias;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) nz[j] = pn[eg + NXE * j < E ? eg + NXE * j : E - 1];
+  }
   double h[TE], s[TE];
   double m = NEG;
 #pragma unroll
   for (int j = 0; j < TE; ++j) {
     const int e = eg + NXE * j;
     const bool ok = e < E;
-    double hv = acc[j] + (bg != nullptr && ok ? (double)bg[e] : 0.0);
-    if (noise != nullptr && live && ok) hv += sigma * (double)noise[t * E + e];
+    double hv = acc[j] + (ok ? (double)rb.g[j] : 0.0);
+    if (noise != nullptr && live && ok) hv += sigma * (double)nz[j];
     h[j] = ok ? hv : NEG;
-    s[j] = ok ? h[j] + (bsel != nullptr ? (double)bsel[e] : 0.0) : NEG;
+    s[j] = ok ? h[j] + (double)rb.s[j] : NEG;
     m = fmax(m, h[j]);
   }
   m = group_max<NXE>(m);
@@ -480,6 +520,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
   const int half = SPLIT ? (tid >> 4) & 1 : 0;
   const int64_t t = (int64_t)blockIdx.x * KS_TPB + tid / (NT / KS_TPB);
   const int row4 = ks_row_float4(d, XBF16);
+  constexpr int TE = (EP >= 16) ? EP / 16 : 1;
+  const RouterBias<TE> rb = load_router_bias<TE, KS_LPT>(bg, bsel, lane, E);  // used in the epilogue
 
   // this lane's slice of the token row, loaded before the W_g fill so both
   // loads are in flight together (at most XV vectors a lane); columns past
@@ -582,7 +624,6 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
   }
 
   // reduce-scatter over the 16 lanes: lane l ends with experts l + 16 j
-  constexpr int TE = (EP >= 16) ? EP / 16 : 1;
   double r[TE];
   if constexpr (EP == 8) {
     double a4[4], a2[2];
@@ -616,13 +657,13 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
       const int64_t tt = (int64_t)blockIdx.x * KS_TPB + tl;
       RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
       token_epilogue<TE, KS_LPT>(rr, lane, tt, tt < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                                 noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+                                 noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
     }
   } else {
     const int tl = tid / KS_LPT;
     RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
     token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                               noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr);
+                               noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
   }
   if (hist16 == nullptr) return;  // uniform
   __syncthreads();
