@@ -9,14 +9,30 @@
 // shared term, then one rounding of the result.
 //
 // One wavefront per token; lanes stride the row in 16-byte vectors.  Lane j < k
-// fetches (row, gate) of choice j once into LDS for the whole wave.
+// fetches (row, gate) of choice j once into LDS for the whole wave; then the
+// rows of all choices (up to 8) load together.
 
 #include "common.h"
 #include "internal.h"
 
 namespace moe {
 
-template <bool BF16>
+template <int EPV>
+__device__ __forceinline__ void unpack_vec(const vec16& q, float (&f)[EPV]) {
+  if constexpr (EPV == 8) {
+    unpack_bf16x8(q, f);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f[u] = __uint_as_float(q.w[u]);
+  }
+}
+
+// KC > 0: k == KC, and every choice's row (and the shared row) is loaded
+// before the first is added, so the wave waits on memory once instead of once
+// a choice.  A dropped choice (row < 0) loads a kept row of the same token and
+// is left out of the sum by a select; a token with no kept row loads none.
+// KC == 0: any k, one choice at a time.  SH: shared_out given.
+template <bool BF16, int KC, bool SH>
 __global__ __launch_bounds__(256) void combine_kernel(const vec16* __restrict__ yd,
                                                       const int32_t* __restrict__ row,
                                                       const float* __restrict__ gate,
@@ -34,33 +50,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const vec16* __restrict__ 
   }
   __syncthreads();
   if (t >= T) return;
+  // KC > 0: this token's choices in registers (entries past k are never
+  // read as rows: they become -1), and a kept row of the token (the same for
+  // the whole wave) or -1
+  constexpr int NC = KC > 0 ? KC : 1;
+  int rr[NC];
+  float gg[NC];
+  int rkept = -1;
+  if constexpr (KC > 0) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int sr = s_row[w][j];
+      gg[j] = s_g[w][j];
+      rr[j] = j < k ? sr : -1;
+    }
+#pragma unroll
+    for (int j = KC - 1; j >= 0; --j) rkept = rr[j] >= 0 ? rr[j] : rkept;
+  }
   for (int64_t v = lane; v < vpr; v += 64) {
+    vec16 qs;
+    if constexpr (SH) qs = ysh[t * vpr + v];
     float acc[EPV];
 #pragma unroll
-    for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = s_row[w][j];
-      const float g = s_g[w][j];
-      if (r >= 0) {
-        const vec16 q = yd[(int64_t)r * vpr + v];
-        float f[EPV];
-        if constexpr (BF16) unpack_bf16x8(q, f);
-        else {
+    for (int u = 0; u < EPV; ++u) acc[u] = 0.f;
+    if constexpr (KC > 0) {
+      if (rkept >= 0) {  // uniform
+        vec16 q[KC];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) f[u] = __uint_as_float(q.w[u]);
+        for (int j = 0; j < KC; ++j) q[j] = yd[(int64_t)(rr[j] >= 0 ? rr[j] : rkept) * vpr + v];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+          float f[EPV];
+          unpack_vec<EPV>(q[j], f);
+#pragma unroll
+          for (int u = 0; u < EPV; ++u) {
+            const float a = fmaf(gg[j], f[u], acc[u]);
+            acc[u] = rr[j] >= 0 ? a : acc[u];
+          }
         }
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int r = s_row[w][j];
+        const float g = s_g[w][j];
+        if (r >= 0) {
+          float f[EPV];
+          unpack_vec<EPV>(yd[(int64_t)r * vpr + v], f);
 #pragma unroll
-        for (int u = 0; u < EPV; ++u) acc[u] = fmaf(g, f[u], acc[u]);
+          for (int u = 0; u < EPV; ++u) acc[u] = fmaf(g, f[u], acc[u]);
+        }
       }
     }
-    if (ysh != nullptr) {
-      const vec16 q = ysh[t * vpr + v];
+    if constexpr (SH) {
       float f[EPV];
-      if constexpr (BF16) unpack_bf16x8(q, f);
-      else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) f[u] = __uint_as_float(q.w[u]);
-      }
+      unpack_vec<EPV>(qs, f);
 #pragma unroll
       for (int u = 0; u < EPV; ++u) acc[u] += f[u];
     }
@@ -80,12 +123,36 @@ hipError_t launch_combine(const void* expert_out, const int32_t* row, const floa
   if (T <= 0) return hipSuccess;
   const int64_t vpr = (int64_t)d_out * (bf16 ? 2 : 4) / 16;
   const dim3 grid((unsigned)((T + 3) / 4));
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st, (const vec16*)expert_out, row,
-                       gate, (const vec16*)shared_out, T, k, vpr, (vec16*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, st, (const vec16*)expert_out, row,
-                       gate, (const vec16*)shared_out, T, k, vpr, (vec16*)y);
+  const vec16* yd = (const vec16*)expert_out;
+  const vec16* ys = (const vec16*)shared_out;
+  vec16* yo = (vec16*)y;
+#define MOE_COMBINE(B, KC, SH) \
+  hipLaunchKernelGGL((combine_kernel<B, KC, SH>), grid, dim3(256), 0, st, yd, row, gate, ys, T, k, vpr, yo)
+#define MOE_COMBINE_SH(B, KC)                 \
+  do {                                        \
+    if (shared_out != nullptr) MOE_COMBINE(B, KC, true); \
+    else MOE_COMBINE(B, KC, false);           \
+  } while (0)
+#define MOE_COMBINE_KC(B)                     \
+  switch (k) {                                \
+    case 1: MOE_COMBINE_SH(B, 1); break;      \
+    case 2: MOE_COMBINE_SH(B, 2); break;      \
+    case 3: MOE_COMBINE_SH(B, 3); break;      \
+    case 4: MOE_COMBINE_SH(B, 4); break;      \
+    case 5: MOE_COMBINE_SH(B, 5); break;      \
+    case 6: MOE_COMBINE_SH(B, 6); break;      \
+    case 7: MOE_COMBINE_SH(B, 7); break;      \
+    case 8: MOE_COMBINE_SH(B, 8); break;      \
+    default: MOE_COMBINE_SH(B, 0); break;     \
+  }
+  if (bf16) {
+    MOE_COMBINE_KC(true);
+  } else {
+    MOE_COMBINE_KC(false);
+  }
+#undef MOE_COMBINE_KC
+#undef MOE_COMBINE_SH
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ SCALED = {
     "noisy_mfma": synth.LARGE_CREDIT.with_(T=1024, d=512, F=384, router_noise=0.5),
     "mlp_gate": synth.DEFAULT.with_(T=1000, d=136, F=72, E=12, k=3, mlp_gate=128, capacity_factor=Fraction(3, 2)),
     "mlp_gate_noisy_fp32": synth.TINY.with_(T=300, d=40, F=24, E=6, k=2, mlp_gate=32, router_noise=0.2),
+    # more than eight choices a token (the combine's one-choice-at-a-time path), many dropped
+    "wide_topk": synth.DEFAULT.with_(T=600, d=64, F=32, E=16, k=10, capacity_factor=Fraction(3, 4)),
 }
 
 
