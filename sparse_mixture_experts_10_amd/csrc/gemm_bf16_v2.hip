@@ -90,15 +90,29 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   // physical chunk l % (4 SUB), so each 4 SUB lanes fetch one row's 64 SUB
   // contiguous bytes.  Rows past BM + BN (the surplus instructions) read a
   // clamped weight row into the dummy slot.
+  // Gathered rows: every slot's row index is loaded before any address is
+  // formed (weight slots load the tile's first index, unused), so the loads
+  // share one wait; loaded under the per-slot branch each got its own.
+  int64_t arow[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
+    arow[i] = tl.row0 + (row < BM ? (row < tl.M ? row : tl.M - 1) : 0);
+  }
+  if (p.a_rows != nullptr) {  // uniform
+    int ai[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) ai[i] = p.a_rows[arow[i]];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) arow[i] = ai[i];
+  }
   const bf16_t* src[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
     const int chunk = (lane % (4 * SUB)) ^ swz<SUB>(row);  // logical chunk stored here
     if (row < BM) {
-      const int r = row < tl.M ? row : tl.M - 1;
-      const int64_t arow = p.a_rows ? (int64_t)p.a_rows[tl.row0 + r] : tl.row0 + r;
-      src[i] = A + arow * K + chunk * 8;
+      src[i] = A + arow[i] * K + chunk * 8;
     } else {
       const int nr = row - BM;
       const int n = (n0 + nr < N) ? n0 + nr : N - 1;
@@ -132,6 +146,24 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   // operand read offsets (bytes within a stage): lane (fr, fc) reads row fr
   // of its 16-row tile at logical k-chunk 4 h + fc of sub-slab h
   const int fr = lane & 15, fc = lane >> 4;
+
+  // this lane's bias columns (four bf16 per N tile; unsegmented bias), all
+  // loaded together (columns past N read column N - 4, unused): before the K
+  // loop when the register budget allows (at most four waves a SIMD), so the
+  // epilogue does not wait on them, else at the start of the epilogue
+  constexpr bool BIAS_EARLY = MINB * ((NW + 3) / 4) <= 4;
+  const bf16_t* bias = (const bf16_t*)p.bias;
+  uint2 bpre[TN];
+  auto load_bias = [&]() {
+    if (!SEG && bias != nullptr) {  // uniform
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * C::WN + j * 16 + fc * 4;
+        bpre[j] = *(const uint2*)(bias + (int64_t)tl.g * N + (n < N ? n : N - 4));
+      }
+    }
+  };
+  if constexpr (BIAS_EARLY) load_bias();
   int a_rd[SUB][TM], b_rd[SUB][TN];
 #pragma unroll
   for (int h = 0; h < SUB; ++h) {
@@ -236,7 +268,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   // ---- epilogue: lane holds C[wm*WM + i*16 + fr][wn*WN + j*16 + 4*fc + r] ----
   // (the weight operand goes first, so each lane holds four consecutive
   // columns of one row; N % 8 == 0 puts all four in range or none)
-  const bf16_t* bias = (const bf16_t*)p.bias;
+  if constexpr (!BIAS_EARLY) load_bias();
   float bcol[TN][4];
   bool ncol_ok[TN];
 #pragma unroll
@@ -251,7 +283,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) bcol[j][r] += bf16_to_f32(bias[(int64_t)q * N + n + r]);
       } else {
-        const uint2 bb = *(const uint2*)(bias + (int64_t)tl.g * N + n);
+        const uint2 bb = bpre[j];
         bcol[j][0] = __uint_as_float(bb.x << 16);
         bcol[j][1] = __uint_as_float(bb.x & 0xffff0000u);
         bcol[j][2] = __uint_as_float(bb.y << 16);

@@ -36,15 +36,21 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ goff, int 
     } else {
       gpl = (G + 63) / 64;  // groups per lane (<= 4: at most 256 groups)
       g0 = lane * gpl;
+      // every offset load goes out before any is used (groups clamped to
+      // G - 1, dropped afterwards): under the per-group branch each load got
+      // a wait of its own
+      int lo[4], hi[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int g = g0 + q;
-        gs[q] = 0;
-        gm[q] = 0;
-        if (q < gpl && g < G) {
-          gs[q] = goff[g];
-          gm[q] = goff[g + 1] - gs[q];
-        }
+        const int g = g0 + q < G ? g0 + q : G - 1;
+        lo[q] = goff[g];
+        hi[q] = goff[g + 1];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool own = q < gpl && g0 + q < G;
+        gs[q] = own ? lo[q] : 0;
+        gm[q] = own ? hi[q] - lo[q] : 0;
         local += (gm[q] + BM - 1) / BM;
       }
       incl = local;
