@@ -118,6 +118,38 @@ __device__ __forceinline__ float act_static(float z) {
   else return z;
 }
 
+// Exchange with lane ^ M.  Inside a 16-lane row this is DPP (quad permutes for
+// M = 1, 2; row rotates for M = 4, 8), a plain VALU move; M >= 16 goes
+// through ds_bpermute.  Every lane must be active.
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    // rotate the row by 4 one way or the other: each lane keeps the rotation
+    // that brings it lane ^ 4 (decided from the lane ids themselves)
+    const int lid = (int)__lane_id();
+    const int a = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    const int b = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, false);  // row_ror:12
+    const int src_a = __builtin_amdgcn_update_dpp(0, lid, 0x124, 0xF, 0xF, false);
+    return src_a == (lid ^ 4) ? a : b;
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8 (= lane ^ 8)
+  } else {
+    return __shfl_xor(v, M, 64);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ double xor_lane_d(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = xor_lane<M>((int)(u & 0xffffffffll));
+  const int hi = xor_lane<M>((int)(u >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));

@@ -152,11 +152,15 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
   s_red[tid] = s;
   if (nparts <= 64) {
     if (tid < 64) {
-#pragma unroll
-      for (int w = 32; w > 0; w >>= 1) {
-        const double o = __shfl_down(z, w, 64);
-        if (w < nparts) z += o;
-      }
+      // lane 0 adds lane w at each level; for the lanes i < w that feed lane
+      // 0, lane i ^ w is lane i + w, so the exchange is lane ^ w (a DPP move
+      // below 16 instead of an LDS round trip); levels past nparts are skipped
+      if (32 < nparts) z += xor_lane_d<32>(z);
+      if (16 < nparts) z += xor_lane_d<16>(z);
+      if (8 < nparts) z += xor_lane_d<8>(z);
+      if (4 < nparts) z += xor_lane_d<4>(z);
+      if (2 < nparts) z += xor_lane_d<2>(z);
+      if (1 < nparts) z += xor_lane_d<1>(z);
       if (tid == 0) s_z[0] = z;
     }
     __syncthreads();
@@ -195,7 +199,14 @@ __device__ __forceinline__ void stats_finish_write(const int32_t* count, int64_t
   double fp = 0.0;
   if (E <= 64) {
     if (tid >= 64) return;  // wave 0 holds every product
-    for (int ee = 0; ee < E; ++ee) fp += __shfl(fp_e, ee, 64);
+    // lane ee's product read into scalar registers (no LDS round trip)
+    const long long u = __double_as_longlong(fp_e);
+    const int lo = (int)(u & 0xffffffffll), hi = (int)(u >> 32);
+    for (int ee = 0; ee < E; ++ee) {
+      const unsigned l = (unsigned)__builtin_amdgcn_readlane(lo, ee);
+      const long long h = __builtin_amdgcn_readlane(hi, ee);
+      fp += __longlong_as_double((h << 32) | l);
+    }
   } else {
     __syncthreads();
     if (tid < E) s_red[tid] = fp_e;
