@@ -113,11 +113,15 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
   const int Q = 256 / E;
   double s = 0.0, z = 0.0;
   const int e = tid % E, q = tid / E;
+  // the wave that holds the lse^2 group sums (lane i: group i)
+  int zw = 0;
   if (nsub > 0 && nparts <= Q) {
-    // at most one group a thread in either sum: both groups' sub-partials
-    // are loaded before either is added up
-    const bool has_e = q < nparts, has_z = tid < nparts;
-    const int64_t re = (int64_t)q * kStatsSubs, rz = (int64_t)tid * kStatsSubs;
+    // at most one group a thread in either sum, the lse^2 groups in wave 3
+    // (the expert groups fill the first waves): every sub-partial is loaded
+    // before any is added up
+    zw = 3;
+    const bool has_e = q < nparts, has_z = tid >= 192 && tid - 192 < nparts;
+    const int64_t re = (int64_t)q * kStatsSubs, rz = (int64_t)(tid - 192) * kStatsSubs;
     double ve[kStatsSubs], vz[kStatsSubs];
 #pragma unroll
     for (int i = 0; i < kStatsSubs; ++i) {
@@ -151,7 +155,7 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
   }
   s_red[tid] = s;
   if (nparts <= 64) {
-    if (tid < 64) {
+    if ((tid >> 6) == zw) {  // uniform per wave
       // lane 0 adds lane w at each level; for the lanes i < w that feed lane
       // 0, lane i ^ w is lane i + w, so the exchange is lane ^ w (a DPP move
       // below 16 instead of an LDS round trip); levels past nparts are skipped
@@ -161,7 +165,7 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
       if (4 < nparts) z += xor_lane_d<4>(z);
       if (2 < nparts) z += xor_lane_d<2>(z);
       if (1 < nparts) z += xor_lane_d<1>(z);
-      if (tid == 0) s_z[0] = z;
+      if (tid == 64 * zw) s_z[0] = z;
     }
     __syncthreads();
     return;
