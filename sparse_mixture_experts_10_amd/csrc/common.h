@@ -119,8 +119,8 @@ __device__ __forceinline__ float act_static(float z) {
 }
 
 // Exchange with lane ^ M.  Inside a 16-lane row this is DPP (quad permutes for
-// M = 1, 2; row rotates for M = 4, 8), a plain VALU move; M >= 16 goes
-// through ds_bpermute.  Every lane must be active.
+// M = 1, 2; row rotates for M = 4, 8), a plain VALU move; M = 16, 32 are the
+// permlane swaps, also VALU.  Every lane must be active.
 template <int M>
 __device__ __forceinline__ int xor_lane(int v) {
   if constexpr (M == 1) {
@@ -137,6 +137,13 @@ __device__ __forceinline__ int xor_lane(int v) {
     return src_a == (lid ^ 4) ? a : b;
   } else if constexpr (M == 8) {
     return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8 (= lane ^ 8)
+  } else if constexpr (M == 16 || M == 32) {
+    // gfx950 lane swaps: permlane16_swap(v, v) leaves rows 0, 2 with their own
+    // value in the first result and row 1, 3's in the second (and the other
+    // way round on rows 1, 3); permlane32_swap likewise for the two halves
+    const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false)
+                           : __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(((int)__lane_id() & M) ? p[0] : p[1]);
   } else {
     return __shfl_xor(v, M, 64);
   }

@@ -331,8 +331,8 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     }
     if (want_sq) {
       // the row's 4 fc lanes, then (below) the WGN wave columns in order
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
+      rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
+      rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
       if (fc == 0) s_sq[wn][wm * C::WM + i * 16 + fr] = rs;
     }
     __syncthreads();

@@ -33,6 +33,10 @@ SCALED = {
     "mlp_gate_noisy_fp32": synth.TINY.with_(T=300, d=40, F=24, E=6, k=2, mlp_gate=32, router_noise=0.2),
     # more than eight choices a token (the combine's one-choice-at-a-time path), many dropped
     "wide_topk": synth.DEFAULT.with_(T=600, d=64, F=32, E=16, k=10, capacity_factor=Fraction(3, 4)),
+    # the fused statistics finish over 24 and 47 groups of 256 tokens (tree levels
+    # 16 and 32 of its lse^2 sum)
+    "stats_groups_24": synth.DEFAULT.with_(T=6000, d=64, F=32),
+    "stats_groups_47": synth.DEFAULT.with_(T=12000, d=64, F=32),
 }
 
 
@@ -62,7 +66,8 @@ def test_layer_materialised_dispatch_matches_oracle(name):
     check_layer(inp, o)
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "switch_zipf_s", "fine_shared_s", "large_credit_s"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "switch_zipf_s", "fine_shared_s", "large_credit_s",
+                                  "stats_groups_24", "stats_groups_47"])
 def test_fused_route_equals_separate_calls(name):
     """moe_route (router, index-only dispatch and statistics in one call) gives
     the same bits as moe_router_topk + moe_dispatch + moe_route_stats."""
