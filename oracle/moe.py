@@ -6,6 +6,8 @@ The pass, step by step, with the passage each step follows:
   1. router logits h = W_g x (+ router bias)       [Appendix C, Core MoE symbols; SER, gating path]
      or the optional MLP gate, plus the optional training noise of noisy top-k
                                                     [SER, Configuration; gating path]
+     and the gate temperature tau, which divides those logits
+                                                    [SER, gating path: gate_forward takes a temperature]
   2. P = softmax(h), lse = log sum_i e^{h_i}       [Appendix C, Core MoE symbols; Balancing (z-loss)]
   3. T_k(x) = the k experts with the highest scores, score = h + b_sel
                                                     [Appendix C, Core MoE symbols and Balancing (b_i);
@@ -100,6 +102,23 @@ def noisy_logits(h: np.ndarray, noise: np.ndarray, sigma: float) -> np.ndarray:
     selection, gates, statistics).
     """
     return np.asarray(h, np.float64) + float(sigma) * np.asarray(noise, np.float64)
+
+
+def tempered_logits(h: np.ndarray, tau: float) -> np.ndarray:
+    """h / tau: the gate's logits at temperature tau > 0.
+
+    [SER, gating path: the gate-forward call takes a temperature argument
+    and applies a softmax to the gate logits]  The page names the argument
+    only.  Readings: the usual softmax temperature, dividing the logits (after
+    any training noise) by tau; the tempered logits replace the logits for
+    everything after them (the logits output, softmax, lse and z-loss,
+    selection with the selection bias added to them, gates, statistics).
+    tau = 1 leaves the pass unchanged.
+    """
+    tau = float(tau)
+    if not (tau > 0.0 and math.isfinite(tau)):
+        raise ValueError("temperature must be a finite positive number")
+    return np.asarray(h, np.float64) / tau
 
 
 def softmax_lse(h: np.ndarray):
@@ -344,6 +363,8 @@ def forward(inp: Inputs, tokens: Optional[Sequence[int]] = None,
         h = router_logits(x, inp.W_g, inp.b_g)
     if w.router_noise is not None:
         h = noisy_logits(h, inp.noise, w.router_noise)
+    if w.temperature != 1.0:
+        h = tempered_logits(h, w.temperature)
     P, lse = softmax_lse(h)
     idx = topk(h, k, inp.b_sel) if topk_override is None else np.asarray(topk_override, np.int64)
     gap = near_tie_gap(h, k, inp.b_sel)

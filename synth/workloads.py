@@ -57,6 +57,8 @@ class Workload:
     # router form: 0 = linear router W_g x + b_g; H > 0 = MLP gate of hidden
     # width H (its weights are inputs gW1 [H, d], gb1 [H], gW2 [E, H], gb2 [E])
     mlp_gate: int = 0
+    # gate temperature tau > 0 (1 = none): the gate's logits are divided by it
+    temperature: float = 1.0
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
