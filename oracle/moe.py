@@ -404,3 +404,31 @@ def forward(inp: Inputs, tokens: Optional[Sequence[int]] = None,
     if w.credit:
         res.credit, res.mean_credit = credit(g, disp.row, idx, sqn, E, T, tok)
     return res
+
+
+def expert_rows(inp: Inputs, res: OracleResult, e: int, token_loss: Optional[np.ndarray] = None):
+    """Every kept row of expert e in full: the expert outputs and ||hidden||^2 of
+    its packed rows, its mean credit and (with per-token losses) its
+    expert-attributed loss.
+
+    The same steps as ``forward`` restricted to one expert, for batches too
+    large to evaluate whole: [SER, gating path] the two-layer expert on the
+    rows dispatched to it; [Credit, panel (b)] credit g ||a||_2 per kept
+    choice and the per-expert sums (1/N) sum c (and (1/N) sum c l_j), N = T.
+    ``res`` supplies the routing and dispatch (e.g. forward(inp, tokens=[])).
+    Returns (rows, out [n, d], sqnorm [n], mean_credit_e, expert_loss_e or None).
+    """
+    w = inp.workload
+    dt = w.dtype
+    r0, r1 = int(res.disp.offset[e]), int(res.disp.offset[e + 1])
+    rows = np.arange(r0, r1)
+    tok = res.disp.row_token[r0:r1]
+    ch = res.disp.row_choice[r0:r1]
+    xr = widen(inp.x, dt)[tok]
+    out, a = expert_ffn(xr, widen(inp.W1[e], dt), widen(inp.b1[e], dt),
+                        widen(inp.W2[e], dt), widen(inp.b2[e], dt), w.act)
+    sq = (a * a).sum(axis=1)
+    c = res.topk_gate[tok, ch] * np.sqrt(sq)
+    mean_c = float(c.sum()) / w.T
+    loss = None if token_loss is None else float((c * np.asarray(token_loss, np.float64)[tok]).sum()) / w.T
+    return rows, out, sq, mean_c, loss

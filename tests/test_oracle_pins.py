@@ -421,3 +421,38 @@ def test_topk_override_rewires_dispatch():
     assert (r2.topk_idx == idx).all()
     np.testing.assert_allclose(r2.topk_gate[0], r.topk_gate[0][::-1], atol=1e-15)
     np.testing.assert_allclose(r2.y, r.y, atol=1e-13)   # same set: same output
+
+
+def test_expert_rows_hand_example():
+    """The per-expert evaluation on the hand example: expert 2 holds token 0
+    (choice 1, gate 2/5) and token 1 (choice 1, gate 1/2); with W1 = I, ReLU,
+    W2 = 3 I its rows are 3 x_t, ||a||^2 = 1, mean credit (2/5 + 1/2) / 2 =
+    9/20, and with per-token losses (2, 4) the expert loss (2/5 * 2 + 1/2 * 4) / 2
+    = 7/5 [Credit, panel (b)]."""
+    inp = _hand_example()
+    res = oracle.forward(inp, tokens=[])
+    rows, out, sq, mc, loss = oracle.expert_rows(inp, res, 2, token_loss=np.array([2.0, 4.0]))
+    assert rows.tolist() == [2, 3]
+    np.testing.assert_allclose(out, [[3, 0, 0], [0, 3, 0]], atol=1e-15)
+    np.testing.assert_allclose(sq, [1.0, 1.0], atol=1e-15)
+    assert mc == pytest.approx(9 / 20, rel=1e-14)
+    assert loss == pytest.approx(7 / 5, rel=1e-14)
+
+
+@pytest.mark.parametrize("w", [synth.LARGE_CREDIT.with_(T=96, d=32, F=48, E=6, k=3),
+                               synth.SWITCH_ZIPF.with_(T=200, d=32, F=24, E=8, k=1, credit=True)])
+def test_expert_rows_matches_whole_pass(w):
+    """Expert by expert, the restricted evaluation reproduces the whole pass's
+    expert outputs, ||hidden||^2, mean credit and expert-attributed loss."""
+    inp = synth.draw(w)
+    full = oracle.forward(inp)
+    tl = synth.token_losses(w).astype(np.float64)
+    want_loss = oracle.expert_attributed_loss(full.credit, full.topk_idx, tl, w.E)
+    res = oracle.forward(inp, tokens=[])
+    for e in range(w.E):
+        rows, out, sq, mc, loss = oracle.expert_rows(inp, res, e, token_loss=tl)
+        for i, r in enumerate(rows):
+            np.testing.assert_allclose(out[i], full.expert_out[r], rtol=1e-13, atol=1e-13)
+            assert sq[i] == pytest.approx(full.sqnorm[r], rel=1e-13)
+        assert mc == pytest.approx(full.mean_credit[e], rel=1e-12, abs=1e-300)
+        assert loss == pytest.approx(want_loss[e], rel=1e-12, abs=1e-300)
