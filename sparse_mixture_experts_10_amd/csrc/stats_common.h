@@ -115,9 +115,11 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
   const int e = tid % E, q = tid / E;
   // the wave that holds the lse^2 group sums (lane i: group i)
   int zw = 0;
-  if (nsub > 0 && nparts <= Q) {
+  if (nsub > 0 && nparts <= Q && nparts <= 64) {
     // at most one group a thread in either sum, the lse^2 groups in wave 3
-    // (the expert groups fill the first waves): every sub-partial is loaded
+    // (the expert groups fill the first waves; wave 3 has room for 64
+    // groups, so more groups, possible when E <= 3, take the general path
+    // below, which pairs the same entries): every sub-partial is loaded
     // before any is added up
     zw = 3;
     const bool has_e = q < nparts, has_z = tid >= 192 && tid - 192 < nparts;
