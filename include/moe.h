@@ -79,7 +79,7 @@ extern "C" {
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version, currently 1. */
+/* ABI version, currently 2 (2 added the gate temperature to the router calls). */
 int moe_version(void);
 
 /*
@@ -118,7 +118,13 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
  *            before selection).  The logits become h + noise_std * noise and
  *            everything below uses them.  noise holds standard-normal draws
  *            supplied by the caller; NULL = greedy.
- *   logits   [T, E] fp32 out: h (without b_sel)
+ *   temperature  gate temperature tau, finite and > 0 (1 = none; "Code
+ *            Walkthrough -- SER", The gating / routing path: the gate-forward
+ *            call takes a temperature).  The logits are divided by it after
+ *            the noise, z = (h + noise_std * noise) / tau, in fp64, and z
+ *            replaces h everywhere below: the stored logits, lse, the
+ *            selection on z + b_sel, the gates.  Otherwise MOE_ERR_INVALID_ARG.
+ *   logits   [T, E] fp32 out: the (noisy, tempered) h, without b_sel
  *   lse      [T] fp32 out: log sum_e exp(h_e)
  *   topk_idx [T, k] int32 out: selected experts ordered by (h + b_sel desc,
  *            index asc); equal scores go to the lower index
@@ -134,9 +140,8 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
  */
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
                     const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
-                    float noise_std, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
-                    void* ws, size_t ws_bytes,
-                    hipStream_t stream);
+                    float noise_std, float temperature, float* logits, float* lse, int32_t* topk_idx,
+                    float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Dispatch in token order under capacity `capacity` (>= 0, or -1 = no cap).
@@ -169,8 +174,8 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
  * use_mlp_gater with gater_hidden_dim; The gating / routing path: the logits
  * come from the linear router or the MLP gate):
  *   h = gW2 relu(gW1 x + gb1) + gb2   (hidden width H, evaluated in fp64)
- * then softmax, lse, top-k and gates exactly as moe_router_topk (b_sel and
- * noise likewise).
+ * then softmax, lse, top-k and gates exactly as moe_router_topk (b_sel, noise
+ * and temperature likewise).
  *   gW1 [H, d], gb1 [H] or NULL, gW2 [E, H], gb2 [E] or NULL: fp32 device
  *   H % 8 == 0, H <= 256
  *   ws  MOE_OP_MLP_ROUTER workspace (the fp64 hidden layer, T x H).
@@ -179,8 +184,8 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
 int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* gW1,
                         const float* gb1, int32_t H, const float* gW2, const float* gb2,
                         const float* b_sel, int32_t E, int32_t k, const float* noise, float noise_std,
-                        float* logits, float* lse, int32_t* topk_idx, float* topk_gate, void* ws,
-                        size_t ws_bytes, hipStream_t stream);
+                        float temperature, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * The whole routing half of the layer in one call: moe_router_topk, then an
@@ -189,8 +194,8 @@ int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const 
  * to those three calls.  ("Appendix C -- Acronyms & Symbols", Core MoE symbols,
  * Balancing, Capacity & communication; "Code Walkthrough -- SER", The gating /
  * routing path and Load balancing.)
- *   x, W_g, b_g, b_sel, noise, noise_std, logits, lse, topk_idx, topk_gate:
- *        as moe_router_topk
+ *   x, W_g, b_g, b_sel, noise, noise_std, temperature, logits, lse, topk_idx,
+ *        topk_gate: as moe_router_topk
  *   capacity, expert_count, expert_offset, slot, row, row_token: as moe_dispatch
  *   alpha, beta, f, P, losses: as moe_route_stats
  *   ws   MOE_OP_ROUTE workspace (256-byte aligned).
@@ -198,11 +203,10 @@ int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const 
  */
 int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
               const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
-              float noise_std, int64_t capacity, float alpha, float beta, float* logits, float* lse,
-              int32_t* topk_idx,
-              float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
-              int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
-              size_t ws_bytes, hipStream_t stream);
+              float noise_std, float temperature, int64_t capacity, float alpha, float beta,
+              float* logits, float* lse, int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+              int32_t* expert_offset, int32_t* slot, int32_t* row, int32_t* row_token, float* f,
+              float* P, float* losses, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Grouped expert FFN over packed rows: for every group g and every row r in

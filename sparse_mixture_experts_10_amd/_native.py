@@ -16,19 +16,19 @@ _INT = ctypes.c_int
 _F32 = ctypes.c_float
 _SZ = ctypes.c_size_t
 
-# name -> (restype, argtypes); mirrors include/moe.h
+# name -> (restype, argtypes); mirrors include/moe.h and include/moe_calib.h
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_INT]),
     "moe_version": (_INT, []),
     "moe_capacity": (_INT, [_I64, _I64, _I32, _I64, _I32, ctypes.POINTER(_I64)]),
     "moe_workspace_bytes": (_INT, [_INT, _I64, _I32, _I32, _I32, _I32, _I64, ctypes.POINTER(_SZ)]),
-    "moe_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _P, _P, _P, _P,
-                               _P, _SZ, _P]),
+    "moe_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _F32, _P, _P, _P,
+                               _P, _P, _SZ, _P]),
     "moe_mlp_router_topk": (_INT, [_P, _INT, _I64, _I32, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _F32,
-                                   _P, _P, _P, _P, _P, _SZ, _P]),
+                                   _F32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (_INT, [_P, _I64, _I32, _I32, _I64, _P, _INT, _I32, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
-    "moe_route": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _I64, _F32, _F32]
+    "moe_route": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _F32, _I64, _F32, _F32]
                   + [_P] * 12 + [_P, _SZ, _P]),
     "moe_grouped_ffn": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P,
                                _P, _P, _P, _P, _SZ, _P]),
@@ -43,6 +43,10 @@ SIGNATURES = {
     "moe_balance_losses": (_INT, [_P, _P, _P, _P, _I64, _I32, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]),
     "moe_selection_bias_update": (_INT, [_P, _I32, _I32, _I64, _F32, _P, _P]),
     "moe_dro_update": (_INT, [_P, _I32, _F32, _F32, _P, _P, _P, _P]),
+    # measurement support (include/moe_calib.h)
+    "moe_calib_copy": (_INT, [_P, _P, _SZ, _P]),
+    "moe_calib_read": (_INT, [_P, _SZ, _P, _P]),
+    "moe_calib_mfma": (_INT, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None

@@ -82,24 +82,24 @@ def moe_workspace_bytes(op: int, T: int = 0, d: int = 0, E: int = 1, k: int = 1,
 
 
 def moe_router_topk(x, W_g, b_g, b_sel, k, logits, lse, topk_idx, topk_gate, ws=None, stream=None,
-                    noise=None, noise_std=0.0):
+                    noise=None, noise_std=0.0, temperature=1.0):
     T, d = x.shape
     E = W_g.shape[0]
     wp, wn = _ws(ws)
     _check("moe_router_topk", load().moe_router_topk(
-        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, _p(logits), _p(lse),
-        _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, temperature,
+        _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
 
 
 def moe_mlp_router_topk(x, gW1, gb1, gW2, gb2, b_sel, k, logits, lse, topk_idx, topk_gate, ws, stream=None,
-                        noise=None, noise_std=0.0):
+                        noise=None, noise_std=0.0, temperature=1.0):
     T, d = x.shape
     H = gW1.shape[0]
     E = gW2.shape[0]
     wp, wn = _ws(ws)
     _check("moe_mlp_router_topk", load().moe_mlp_router_topk(
         _p(x), _dt(x), T, d, _p(gW1), _p(gb1), H, _p(gW2), _p(gb2), _p(b_sel), E, k, _p(noise), noise_std,
-        _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
+        temperature, _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), wp, wn, _s(stream)))
 
 
 def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, row, row_token,
@@ -115,12 +115,13 @@ def moe_dispatch(topk_idx, E, capacity, x, expert_count, expert_offset, slot, ro
 
 def moe_route(x, W_g, b_g, b_sel, k, capacity, alpha, beta, logits, lse, topk_idx, topk_gate,
               expert_count, expert_offset, slot, row, row_token, f, P, losses, ws, stream=None, noise=None,
-              noise_std=0.0):
+              noise_std=0.0, temperature=1.0):
     T, d = x.shape
     E = W_g.shape[0]
     wp, wn = _ws(ws)
     _check("moe_route", load().moe_route(
-        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, capacity, alpha, beta,
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, temperature, capacity,
+        alpha, beta,
         _p(logits),
         _p(lse), _p(topk_idx), _p(topk_gate), _p(expert_count), _p(expert_offset), _p(slot), _p(row),
         _p(row_token), _p(f), _p(P), _p(losses), wp, wn, _s(stream)))
@@ -201,3 +202,19 @@ def moe_selection_bias_update(expert_count, k, T, gamma, b_sel, stream=None):
 def moe_dro_update(expert_loss, ema_decay, eta, ema, mu, dro_loss, stream=None):
     _check("moe_dro_update", load().moe_dro_update(
         _p(expert_loss), expert_loss.shape[0], ema_decay, eta, _p(ema), _p(mu), _p(dro_loss), _s(stream)))
+
+
+# measurement support (include/moe_calib.h): not part of the layer
+def moe_calib_copy(src, dst, nbytes, stream=None):
+    _check("moe_calib_copy", load().moe_calib_copy(_p(src), _p(dst), nbytes, _s(stream)))
+
+
+def moe_calib_read(src, nbytes, sink, stream=None):
+    _check("moe_calib_read", load().moe_calib_read(_p(src), nbytes, _p(sink), _s(stream)))
+
+
+def moe_calib_mfma(blocks, iters, sink, stream=None) -> float:
+    """Enqueue the MFMA loop; returns the dense bf16 flops it performs."""
+    fl = ctypes.c_double(0)
+    _check("moe_calib_mfma", load().moe_calib_mfma(blocks, iters, _p(sink), ctypes.byref(fl), _s(stream)))
+    return fl.value

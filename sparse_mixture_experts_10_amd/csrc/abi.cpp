@@ -29,6 +29,9 @@ inline int check_ek(int32_t E, int32_t k) {
   return MOE_OK;
 }
 
+// gate temperature: finite and positive
+inline bool temperature_ok(float tau) { return tau > 0.f && tau <= 3.402823466e38f; }
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // dispatch scratch: chunk counts, group counts (and statistics partials)
@@ -118,7 +121,7 @@ const char* moe_status_string(int status) {
   }
 }
 
-int moe_version(void) { return 1; }
+int moe_version(void) { return 2; }
 
 int moe_capacity(int64_t cf_num, int64_t cf_den, int32_t k, int64_t T, int32_t E,
                  int64_t* capacity) {
@@ -179,10 +182,10 @@ int moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t E, int32_t k, int3
 
 int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
                     const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
-                    float noise_std, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
-                    void* ws, size_t ws_bytes, hipStream_t stream) {
+                    float noise_std, float temperature, float* logits, float* lse, int32_t* topk_idx,
+                    float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
-  if (T < 0 || d < 1 || d % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || d < 1 || d % 8 != 0 || !temperature_ok(temperature)) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -193,16 +196,18 @@ int moe_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const floa
     if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
   }
   return hip_status(launch_router(x, x_dtype == MOE_BF16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
-                                  topk_idx, topk_gate, noise, (double)noise_std, ws, stream));
+                                  topk_idx, topk_gate, noise, (double)noise_std, (double)temperature, ws,
+                                  stream));
 }
 
 int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const float* gW1,
                         const float* gb1, int32_t H, const float* gW2, const float* gb2,
                         const float* b_sel, int32_t E, int32_t k, const float* noise, float noise_std,
-                        float* logits, float* lse, int32_t* topk_idx, float* topk_gate, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        float temperature, float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
   if (T < 0 || d < 1 || d % 8 != 0 || H < 1 || H % 8 != 0) return MOE_ERR_INVALID_ARG;
+  if (!temperature_ok(temperature)) return MOE_ERR_INVALID_ARG;
   if (H > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
@@ -212,8 +217,8 @@ int moe_mlp_router_topk(const void* x, int x_dtype, int64_t T, int32_t d, const 
   const size_t need = mlp_router_ws_bytes(T, H);
   if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0) return MOE_ERR_WORKSPACE;
   return hip_status(launch_mlp_router(x, x_dtype == MOE_BF16, T, d, gW1, gb1, H, gW2, gb2, b_sel, E, k,
-                                      logits, lse, topk_idx, topk_gate, noise, (double)noise_std, ws,
-                                      stream));
+                                      logits, lse, topk_idx, topk_gate, noise, (double)noise_std,
+                                      (double)temperature, ws, stream));
 }
 
 int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64_t capacity,
@@ -240,13 +245,13 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int64
 
 int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
               const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
-              float noise_std, int64_t capacity, float alpha, float beta, float* logits, float* lse,
-              int32_t* topk_idx,
-              float* topk_gate, int32_t* expert_count, int32_t* expert_offset, int32_t* slot,
-              int32_t* row, int32_t* row_token, float* f, float* P, float* losses, void* ws,
-              size_t ws_bytes, hipStream_t stream) {
+              float noise_std, float temperature, int64_t capacity, float alpha, float beta,
+              float* logits, float* lse, int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+              int32_t* expert_offset, int32_t* slot, int32_t* row, int32_t* row_token, float* f,
+              float* P, float* losses, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (int rc = check_ek(E, k)) return rc;
   if (T < 0 || d < 1 || d % 8 != 0 || capacity < -1) return MOE_ERR_INVALID_ARG;
+  if (!temperature_ok(temperature)) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (!expert_count || !expert_offset) return MOE_ERR_INVALID_ARG;
@@ -265,7 +270,8 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
     // two kernels: the counting router, then the scatter
     const DispatchWs w = route_units_layout(ws, T, E);
     const hipError_t e = launch_router_counting(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
-                                                topk_idx, topk_gate, noise, (double)noise_std, w.group,
+                                                topk_idx, topk_gate, noise, (double)noise_std,
+                                                (double)temperature, w.group,
                                                 w.part, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
@@ -274,7 +280,8 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
   const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
   if (T > 0) {
     const hipError_t e = launch_router(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse, topk_idx,
-                                       topk_gate, noise, (double)noise_std, ws, stream);
+                                       topk_gate, noise, (double)noise_std, (double)temperature, ws,
+                                       stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,

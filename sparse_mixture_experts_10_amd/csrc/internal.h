@@ -21,16 +21,17 @@ constexpr int kGemmF32BN = 64;        // N tile of the fp32 grouped GEMM
 constexpr int kGemmF32BM = 64;        // M tile of the fp32 grouped GEMM
 
 // ws: MFMA-path scratch (router_mfma_ws_bytes) when router_uses_mfma(), else unused.
-// noise: [T, E] standard-normal draws added as sigma * noise (or nullptr).
+// noise: [T, E] standard-normal draws added as sigma * noise (or nullptr);
+// tau: gate temperature dividing the (noisy) logits, 1 = none.
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
-                         float* lse, int32_t* idx, float* gate, const float* noise, double sigma,
+                         float* lse, int32_t* idx, float* gate, const float* noise, double sigma, double tau,
                          void* ws, hipStream_t st);
 // MLP gate: hidden [T, H] fp64 in ws (mlp_router_ws_bytes), then the E-split router on it.
 hipError_t launch_mlp_router(const void* x, bool xbf16, int64_t T, int d, const float* gW1,
                              const float* gb1, int H, const float* gW2, const float* gb2,
                              const float* bsel, int E, int k, float* logits, float* lse, int32_t* idx,
-                             float* gate, const float* noise, double sigma, void* ws, hipStream_t st);
+                             float* gate, const float* noise, double sigma, double tau, void* ws, hipStream_t st);
 size_t mlp_router_ws_bytes(int64_t T, int H);
 bool router_uses_mfma(bool xbf16, int d, int E);
 size_t router_mfma_ws_bytes(int64_t T, int d, int E);
@@ -41,7 +42,7 @@ bool router_uses_ksplit(bool xbf16, int d, int E);
 hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                   const float* bg, const float* bsel, int E, int k, float* logits,
                                   float* lse, int32_t* idx, float* gate, const float* noise,
-                                  double sigma, int32_t* hist16, double* p16, hipStream_t st);
+                                  double sigma, double tau, int32_t* hist16, double* p16, hipStream_t st);
 
 // Dispatch scratch: per-chunk counts [nchunks][E], per-group counts
 // [ngroups][E] (a group is kStatsTokens tokens), and, for the fused routing

@@ -135,7 +135,10 @@ __device__ __forceinline__ RouterBias<TE> load_router_bias(const float* __restri
 // (router bias not yet added): lane eg holds experts e = eg + NXE j, j < TE.
 // With noise != nullptr the logits are h + sigma * noise[t, e] (noisy top-k,
 // page "Code Walkthrough -- SER", the gating / routing path: training noise is
-// added to the logits before selection) and everything after uses them.
+// added to the logits before selection), and the gate temperature tau > 0
+// (the same page's gate-forward argument) divides them: z = (h + sigma n) /
+// tau in fp64.  Everything after uses z: the stored logits, lse, selection on
+// z + b_sel, the gates and the statistics.  tau = 1 skips the division.
 // Writes logits, lse, top-k indices and gates for token t (when live).
 // With flag_rel > 0 it returns true (on every lane of the token) when two
 // consecutive scores among the k + 1 highest (k when k = E) are closer than
@@ -149,7 +152,7 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
                                                float* __restrict__ logits, float* __restrict__ lse_out,
                                                int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_gate,
-                                               const float* __restrict__ noise, double sigma,
+                                               const float* __restrict__ noise, double sigma, double tau,
                                                double flag_rel = 0.0, RouterTap* tap = nullptr,
                                                const RouterBias<TE>* pre = nullptr) {
   const double NEG = -__builtin_huge_val();
@@ -172,6 +175,7 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
     const bool ok = e < E;
     double hv = acc[j] + (ok ? (double)rb.g[j] : 0.0);
     if (noise != nullptr && live && ok) hv += sigma * (double)nz[j];
+    if (tau != 1.0) hv = hv / tau;  // uniform
     h[j] = ok ? hv : NEG;
     s[j] = ok ? h[j] + (double)rb.s[j] : NEG;
     m = fmax(m, h[j]);
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
     const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma, double tau) {
   using C = RouterCfg<EP>;
   constexpr int TE = C::TE, NXE = C::NXE, TM = C::TM, BT = C::BT, LDX = C::KC + 1;
   __shared__ XStage<XT> xs[BT * LDX];
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(RouterCfg<EP>::NT) void router_kernel(
   for (int i = 0; i < TM; ++i) {
     const int64_t t = t0 + tg * TM + i;
     token_epilogue<TE, NXE>(acc[i], eg, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx,
-                            topk_gate, noise, sigma);
+                            topk_gate, noise, sigma, tau);
   }
 }
 
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
     const void* __restrict__ xv, int64_t T, int d, const float* __restrict__ Wg,
     const float* __restrict__ bg, const float* __restrict__ bsel, int E, int k,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma,
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma, double tau,
     int32_t* __restrict__ hist16, double* __restrict__ p16) {
   extern __shared__ float4 wsm[];  // W_g, fp32, in the chunked layout above
   // fused routing pass (hist16 != nullptr): this block's 16 tokens as one
@@ -625,13 +629,13 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void router_ksplit_kernel(
       const int64_t tt = (int64_t)blockIdx.x * KS_TPB + tl;
       RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
       token_epilogue<TE, KS_LPT>(rr, lane, tt, tt < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                                 noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
+                                 noise, sigma, tau, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
     }
   } else {
     const int tl = tid / KS_LPT;
     RouterTap tap{tap_p[tl], &tap_lse[tl], tap_hist};
     token_epilogue<TE, KS_LPT>(r, lane, t, t < T, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                               noise, sigma, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
+                               noise, sigma, tau, 0.0, hist16 != nullptr ? &tap : nullptr, &rb);
   }
   if (hist16 == nullptr) return;  // uniform
   __syncthreads();
@@ -665,7 +669,7 @@ template <int EP>
 static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                        const float* bg, const float* bsel, int E, int k,
                                        float* logits, float* lse, int32_t* idx, float* gate,
-                                       const float* noise, double sigma, int32_t* hist16,
+                                       const float* noise, double sigma, double tau, int32_t* hist16,
                                        double* p16, hipStream_t st) {
   const int64_t blocks = (T + KS_TPB - 1) / KS_TPB;
   const dim3 grid((unsigned)blocks);
@@ -674,7 +678,7 @@ static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int
   const bool split = blocks <= kCus;
 #define MOE_KS_LAUNCH(XB, SP)                                                                              \
   hipLaunchKernelGGL((router_ksplit_kernel<EP, XB, SP>), grid, dim3(SP ? 512 : 256), lds, st, x, T, d, Wg, bg, \
-                     bsel, E, k, logits, lse, idx, gate, noise, sigma, hist16, p16)
+                     bsel, E, k, logits, lse, idx, gate, noise, sigma, tau, hist16, p16)
   if (xbf16) {
     if (split) MOE_KS_LAUNCH(true, true);
     else MOE_KS_LAUNCH(true, false);
@@ -726,7 +730,7 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
     const float* __restrict__ part, int64_t T, int E, int k, const float* __restrict__ bg,
     const float* __restrict__ bsel, float* __restrict__ logits, float* __restrict__ lse_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ count,
-    int32_t* __restrict__ list, const float* __restrict__ noise, double sigma) {
+    int32_t* __restrict__ list, const float* __restrict__ noise, double sigma, double tau) {
   constexpr int NXE = (EP >= 256) ? 32 : 16;
   constexpr int TE = EP / NXE;
   const int tid = threadIdx.x;
@@ -744,7 +748,7 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
     acc[j] = a;
   }
   const bool near = token_epilogue<TE, NXE>(acc, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
-                                            topk_idx, topk_gate, noise, sigma, kRefineRel);
+                                            topk_idx, topk_gate, noise, sigma, tau, kRefineRel);
   if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
 }
 
@@ -763,7 +767,7 @@ __global__ __launch_bounds__(64 * NW) void router_mfma_kernel(
     const float* __restrict__ bg, const float* __restrict__ bsel, float* __restrict__ logits,
     float* __restrict__ lse_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     int32_t* __restrict__ count, int32_t* __restrict__ list, const float* __restrict__ noise,
-    double sigma) {
+    double sigma, double tau) {
   constexpr int E = EP;
   constexpr int RW = 16 * NW;          // tokens a block
   constexpr int NR = RW + 3 * E;       // stage rows: the tokens, then hi, mid, lo weight rows
@@ -866,7 +870,7 @@ __global__ __launch_bounds__(64 * NW) void router_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < TE; ++j) a[j] = s_h[tl * E + eg + NXE * j];
     const bool near = token_epilogue<TE, NXE>(a, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
-                                              topk_idx, topk_gate, noise, sigma, kRefineRel);
+                                              topk_idx, topk_gate, noise, sigma, tau, kRefineRel);
     if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
   }
 }
@@ -932,7 +936,7 @@ __global__ __launch_bounds__(256) void router_refine_epilogue_kernel(
     const double* __restrict__ h, const float* __restrict__ bg, const float* __restrict__ bsel, int E,
     int k, const int32_t* __restrict__ count, const int32_t* __restrict__ list,
     float* __restrict__ logits, float* __restrict__ lse_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma) {
+    float* __restrict__ topk_gate, const float* __restrict__ noise, double sigma, double tau) {
   constexpr int TE = (EP + 63) / 64;
   const int n = *count;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -945,7 +949,7 @@ __global__ __launch_bounds__(256) void router_refine_epilogue_kernel(
       acc[j] = e < E ? h[(int64_t)i * E + e] : 0.0;
     }
     token_epilogue<TE, 64>(acc, lane, t, true, E, k, bg, bsel, logits, lse_out, topk_idx, topk_gate,
-                           noise, sigma);
+                           noise, sigma, tau);
   }
 }
 
@@ -964,7 +968,7 @@ template <int EP>
 static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const float* Wg,
                                      const float* bg, const float* bsel, int E, int k,
                                      float* logits, float* lse, int32_t* idx, float* gate,
-                                     const float* noise, double sigma, void* ws, hipStream_t st) {
+                                     const float* noise, double sigma, double tau, void* ws, hipStream_t st) {
   char* w8 = (char*)ws;
   bf16_t* Ws = (bf16_t*)w8;
   w8 += align256((size_t)3 * E * d * sizeof(bf16_t));
@@ -987,7 +991,7 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
     if (E == EP && T >= 64 * 256) {
       hipLaunchKernelGGL((router_mfma_kernel<EP, 4, 4>), dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st,
                          (const bf16_t*)x, T, d, Ws, k, bg, bsel, logits, lse, idx, gate, count, list,
-                         noise, sigma);
+                         noise, sigma, tau);
       fused = true;
     }
   }
@@ -1001,7 +1005,7 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
     constexpr int NXE = (EP >= 256) ? 32 : 16;
     const int64_t tpb = 256 / NXE;
     hipLaunchKernelGGL((router_finish_kernel<EP>), dim3((unsigned)((T + tpb - 1) / tpb)), dim3(256), 0, st,
-                       part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma);
+                       part, T, E, k, bg, bsel, logits, lse, idx, gate, count, list, noise, sigma, tau);
   }
   // the listed tokens' exact logits go into the consumed partials buffer
   // (T E doubles <= T 3E floats)
@@ -1009,7 +1013,7 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   hipLaunchKernelGGL(router_refine_dots_kernel, dim3(1024), dim3(256), 0, st, (const bf16_t*)x, d, Wg, E,
                      count, list, h);
   hipLaunchKernelGGL((router_refine_epilogue_kernel<EP>), dim3(256), dim3(256), 0, st, h, bg, bsel, E, k,
-                     count, list, logits, lse, idx, gate, noise, sigma);
+                     count, list, logits, lse, idx, gate, noise, sigma, tau);
   return hipGetLastError();
 }
 
@@ -1017,27 +1021,27 @@ template <int EP>
 static hipError_t launch_router_ep(const void* x, int xt, int64_t T, int d, const float* Wg,
                                    const float* bg, const float* bsel, int E, int k, float* logits,
                                    float* lse, int32_t* idx, float* gate, const float* noise,
-                                   double sigma, hipStream_t st) {
+                                   double sigma, double tau, hipStream_t st) {
   using C = RouterCfg<EP>;
   const dim3 grid((unsigned)((T + C::BT - 1) / C::BT));
   if (xt == XT_BF16)
     hipLaunchKernelGGL((router_kernel<EP, XT_BF16>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel, E,
-                       k, logits, lse, idx, gate, noise, sigma);
+                       k, logits, lse, idx, gate, noise, sigma, tau);
   else if (xt == XT_F32)
     hipLaunchKernelGGL((router_kernel<EP, XT_F32>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel,
-                       E, k, logits, lse, idx, gate, noise, sigma);
+                       E, k, logits, lse, idx, gate, noise, sigma, tau);
   else
     hipLaunchKernelGGL((router_kernel<EP, XT_F64>), grid, dim3(C::NT), 0, st, x, T, d, Wg, bg, bsel,
-                       E, k, logits, lse, idx, gate, noise, sigma);
+                       E, k, logits, lse, idx, gate, noise, sigma, tau);
   return hipGetLastError();
 }
 
 static hipError_t launch_router_e_split(const void* x, int xt, int64_t T, int d, const float* Wg,
                                         const float* bg, const float* bsel, int E, int k,
                                         float* logits, float* lse, int32_t* idx, float* gate,
-                                        const float* noise, double sigma, hipStream_t st) {
+                                        const float* noise, double sigma, double tau, hipStream_t st) {
 #define MOE_ROUTER_EP(EPV) \
-  return launch_router_ep<EPV>(x, xt, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, st)
+  return launch_router_ep<EPV>(x, xt, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, tau, st)
   if (E <= 8) MOE_ROUTER_EP(8);
   if (E <= 16) MOE_ROUTER_EP(16);
   if (E <= 32) MOE_ROUTER_EP(32);
@@ -1058,9 +1062,9 @@ bool router_uses_ksplit(bool xbf16, int d, int E) {
 hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                                   const float* bg, const float* bsel, int E, int k, float* logits,
                                   float* lse, int32_t* idx, float* gate, const float* noise,
-                                  double sigma, int32_t* hist16, double* p16, hipStream_t st) {
+                                  double sigma, double tau, int32_t* hist16, double* p16, hipStream_t st) {
 #define MOE_ROUTER_KSC(EPV) \
-  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, \
+  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, tau, \
                                    hist16, p16, st)
   if (E <= 8) MOE_ROUTER_KSC(8);
   if (E <= 16) MOE_ROUTER_KSC(16);
@@ -1071,11 +1075,11 @@ hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, c
 
 hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const float* Wg,
                          const float* bg, const float* bsel, int E, int k, float* logits,
-                         float* lse, int32_t* idx, float* gate, const float* noise, double sigma,
+                         float* lse, int32_t* idx, float* gate, const float* noise, double sigma, double tau,
                          void* ws, hipStream_t st) {
   if (router_uses_mfma(xbf16, d, E)) {
 #define MOE_ROUTER_MFMA(EPV) \
-  return launch_router_mfma<EPV>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, ws, st)
+  return launch_router_mfma<EPV>(x, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, tau, ws, st)
     if (E <= 64) MOE_ROUTER_MFMA(64);
     if (E <= 128) MOE_ROUTER_MFMA(128);
     MOE_ROUTER_MFMA(256);
@@ -1083,7 +1087,7 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
   }
   if (router_uses_ksplit(xbf16, d, E)) {
 #define MOE_ROUTER_KS(EPV) \
-  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, \
+  return launch_router_ksplit<EPV>(x, xbf16, T, d, Wg, bg, bsel, E, k, logits, lse, idx, gate, noise, sigma, tau, \
                                    nullptr, nullptr, st)
     if (E <= 8) MOE_ROUTER_KS(8);
     if (E <= 16) MOE_ROUTER_KS(16);
@@ -1092,7 +1096,7 @@ hipError_t launch_router(const void* x, bool xbf16, int64_t T, int d, const floa
 #undef MOE_ROUTER_KS
   }
   return launch_router_e_split(x, xbf16 ? XT_BF16 : XT_F32, T, d, Wg, bg, bsel, E, k, logits, lse, idx,
-                               gate, noise, sigma, st);
+                               gate, noise, sigma, tau, st);
 }
 
 template <int HP>
@@ -1114,7 +1118,7 @@ size_t mlp_router_ws_bytes(int64_t T, int H) { return align256((size_t)T * (size
 hipError_t launch_mlp_router(const void* x, bool xbf16, int64_t T, int d, const float* gW1,
                              const float* gb1, int H, const float* gW2, const float* gb2,
                              const float* bsel, int E, int k, float* logits, float* lse, int32_t* idx,
-                             float* gate, const float* noise, double sigma, void* ws, hipStream_t st) {
+                             float* gate, const float* noise, double sigma, double tau, void* ws, hipStream_t st) {
   double* hidden = (double*)ws;
   hipError_t e;
   if (H <= 8) e = launch_mlp_hidden<8>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
@@ -1125,7 +1129,7 @@ hipError_t launch_mlp_router(const void* x, bool xbf16, int64_t T, int d, const 
   else e = launch_mlp_hidden<256>(x, xbf16, T, d, gW1, gb1, H, hidden, st);
   if (e != hipSuccess) return e;
   return launch_router_e_split(hidden, XT_F64, T, H, gW2, gb2, bsel, E, k, logits, lse, idx, gate, noise,
-                               sigma, st);
+                               sigma, tau, st);
 }
 
 }  // namespace moe

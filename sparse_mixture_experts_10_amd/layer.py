@@ -69,6 +69,7 @@ class MoELayer:
     fused_route: True (default, with gather_rows) takes router, dispatch and
     statistics in one moe_route call; False makes the three calls separately.
     noise, noise_std: noisy top-k, noise [T, E] fp32 standard-normal draws.
+    temperature: gate temperature tau > 0 dividing the (noisy) logits (1 = none).
     mlp_gate: (gW1 [H, d], gb1 [H], gW2 [E, H], gb2 [E]) fp32 to route with the
     MLP gate instead of W_g / b_g (always the separate calls).
     overlap_shared: run the shared experts on a side stream, concurrently with
@@ -79,7 +80,7 @@ class MoELayer:
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
                  gather_rows: bool = True, fused_route: bool = True, noise=None, noise_std: float = 0.0,
-                 mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True):
+                 temperature: float = 1.0, mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
@@ -88,6 +89,7 @@ class MoELayer:
         self.alpha, self.beta, self.credit = alpha, beta, credit
         self.gather_rows = gather_rows
         self.noise, self.noise_std = noise, float(noise_std)
+        self.temperature = float(temperature)
         self.overlap_shared = overlap_shared
         self._side = None
         self.mlp_gate = mlp_gate
@@ -185,16 +187,18 @@ class MoELayer:
         api.moe_route(x, self.W_g, self.b_g, self.b_sel, self.k, o.capacity, self.alpha, self.beta,
                       o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, o.expert_offset, o.slot,
                       o.row, o.row_token, o.f, o.P, o.losses, o.ws_route, stream, noise=self.noise,
-                      noise_std=self.noise_std)
+                      noise_std=self.noise_std, temperature=self.temperature)
 
     def router(self, x, o: MoEOutputs, stream=None) -> None:
         if self.mlp_gate is not None:
             gW1, gb1, gW2, gb2 = self.mlp_gate
             api.moe_mlp_router_topk(x, gW1, gb1, gW2, gb2, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
-                                    o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std)
+                                    o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std,
+                                    temperature=self.temperature)
             return
         api.moe_router_topk(x, self.W_g, self.b_g, self.b_sel, self.k, o.logits, o.lse, o.topk_idx,
-                            o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std)
+                            o.topk_gate, o.ws_router, stream, noise=self.noise, noise_std=self.noise_std,
+                            temperature=self.temperature)
 
     def dispatch(self, x, o: MoEOutputs, stream=None) -> None:
         o.x = x

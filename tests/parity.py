@@ -47,6 +47,7 @@ def build_layer(inp: synth.Inputs, device="cuda", gather_rows=True, fused_route=
                      capacity_factor=w.capacity_factor, b_g=t["b_g"], b_sel=t["b_sel"], shared=shared,
                      alpha=w.alpha, beta=w.beta, credit=w.credit, gather_rows=gather_rows,
                      fused_route=fused_route, noise=t["noise"], noise_std=w.router_noise or 0.0,
+                     temperature=w.temperature,
                      mlp_gate=gate)
     return layer, t["x"]
 

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from parity import build_layer, check_layer, close_out, f64, say
+from parity import CREDIT_REL, build_layer, check_layer, close_out, f64, say
 from sparse_mixture_experts_10_amd import api
 
 pytestmark = pytest.mark.gpu
@@ -37,6 +37,19 @@ SCALED = {
     # 16 and 32 of its lse^2 sum)
     "stats_groups_24": synth.DEFAULT.with_(T=6000, d=64, F=32),
     "stats_groups_47": synth.DEFAULT.with_(T=12000, d=64, F=32),
+    # more statistics groups than one wave's lanes with few experts: 79 groups at
+    # E 2 and 235 at E 1 (the fused finish must take its general path)
+    "stats_groups_79_E2": synth.DEFAULT.with_(T=20000, d=64, F=32, E=2, k=1),
+    "stats_groups_235_E1": synth.DEFAULT.with_(T=60000, d=64, F=32, E=1, k=1, capacity_factor=Fraction(1, 2)),
+    # gate temperature on every router path: K-split (with and without the
+    # selection bias), E-split, split-weight MFMA (with noise) and the MLP gate
+    "tempered_default": synth.DEFAULT.with_(T=1024, temperature=0.5),
+    "tempered_sel_ksplit": synth.FINE_SHARED.with_(T=1024, d=256, F=200, temperature=1.7),
+    "tempered_e_split": synth.DEFAULT.with_(T=700, d=72, F=64, E=100, k=4, capacity_factor=None,
+                                            sel_bias="uniform:0.1", temperature=0.8),
+    "tempered_noisy_mfma": synth.LARGE_CREDIT.with_(T=1024, d=512, F=384, router_noise=0.5, temperature=2.5),
+    "tempered_mlp_gate": synth.DEFAULT.with_(T=1000, d=136, F=72, E=12, k=3, mlp_gate=128,
+                                             capacity_factor=Fraction(3, 2), temperature=0.3),
 }
 
 
@@ -67,7 +80,8 @@ def test_layer_materialised_dispatch_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "switch_zipf_s", "fine_shared_s", "large_credit_s",
-                                  "stats_groups_24", "stats_groups_47"])
+                                  "stats_groups_24", "stats_groups_47", "stats_groups_79_E2",
+                                  "stats_groups_235_E1", "tempered_default", "tempered_noisy_mfma"])
 def test_fused_route_equals_separate_calls(name):
     """moe_route (router, index-only dispatch and statistics in one call) gives
     the same bits as moe_router_topk + moe_dispatch + moe_route_stats."""
@@ -413,17 +427,55 @@ FULL = {
 }
 
 
+def chosen_experts(kept: np.ndarray, capacity) -> list:
+    """The experts whose every row a full-size test compares: the busiest, the
+    smallest non-empty one, a middle one, the last non-empty group and (with a
+    capacity) one whose rows were capped at C."""
+    nz = np.nonzero(kept)[0]
+    pick = [int(np.argmax(kept)), int(nz[np.argmin(kept[nz])]), int(nz[len(nz) // 2]), int(nz[-1])]
+    if capacity is not None:
+        capped = [int(e) for e in nz if kept[e] == capacity and int(e) not in pick]
+        pick += capped[:1]
+    return sorted(set(pick))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled(name):
     """Full-size workloads in the bench launch configuration: routing, dispatch and
-    statistics over the whole batch; expert outputs, y and credit on 48 sampled tokens."""
+    statistics over the whole batch; y and credit on 48 sampled tokens; and every
+    row of four or five chosen experts (every tile of those groups, the ragged
+    last tile included): expert outputs and, with credit, ||hidden||^2, the
+    expert's mean credit and its expert-attributed loss."""
     w = FULL[name]
     inp, layer, x, o = run(w)
     rng = np.random.default_rng(11)
     tokens = sorted(set([0, 1, w.T - 1] + rng.choice(w.T, 45, replace=False).tolist()))
     rep = check_layer(inp, o, tokens=tokens)
     say(f"  flips={rep.flips} notes={rep.notes}")
+
+    ref = rep.ref
+    kept = np.diff(ref.disp.offset)
+    experts = chosen_experts(kept, ref.C)
+    tl = el = None
+    if w.credit:
+        tl = synth.token_losses(w)
+        el = torch.empty(w.E, device="cuda")
+        api.moe_route_stats(o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, w.alpha, w.beta, o.f,
+                            o.P, o.losses, o.sqnorm, o.row, o.expert_offset, o.row_token, o.credit,
+                            o.mean_credit, o.ws_stats, token_loss=torch.as_tensor(tl).cuda(), expert_loss=el)
+        torch.cuda.synchronize()
+    for e in experts:
+        rows, want, sq, mc, loss = oracle.expert_rows(inp, ref, e, None if tl is None else tl.astype(np.float64))
+        got = f64(o.y_disp[int(rows[0]):int(rows[-1]) + 1])
+        maxabs, relf = close_out(got, want, w.dtype, f"expert {e} outputs ({len(rows)} rows)")
+        say(f"  expert {e}: {len(rows)} rows, max-abs {maxabs:.2e}, rel-F {relf:.2e}")
+        if w.credit:
+            gsq = f64(o.sqnorm[int(rows[0]):int(rows[-1]) + 1])
+            err = np.abs(gsq - sq)
+            assert (err <= CREDIT_REL * np.abs(sq)).all(), f"expert {e} sqnorm worst {(err / sq).max():.3e}"
+            assert abs(float(o.mean_credit[e]) - mc) <= CREDIT_REL * abs(mc), f"expert {e} mean credit"
+            assert abs(float(el[e]) - loss) <= CREDIT_REL * abs(loss), f"expert {e} expert loss"
 
 
 def test_graph_replay_matches_eager():
