@@ -53,6 +53,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2)  /* valid but outside this library's limits (dtype, E, k) */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace missing or smaller than moe_workspace_bytes() */
 #define MOE_ERR_HIP (-4)          /* a HIP launch failed */
+#define MOE_ERR_SCRATCH (-5)      /* needs more scratch than the static buffer of moe_route_noalloc holds */
 
 /* Element types. */
 #define MOE_F32 0
@@ -207,6 +208,30 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
               float* logits, float* lse, int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
               int32_t* expert_offset, int32_t* slot, int32_t* row, int32_t* row_token, float* f,
               float* P, float* losses, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_route without a workspace, for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same pass, kernels and bit-identical results as moe_route, with the
+ * scratch in a static device array of MOE_ROUTE_NOALLOC_MAX_BYTES that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments: as moe_route, without ws and ws_bytes.
+ *   Returns MOE_ERR_SCRATCH, enqueuing nothing, when the call would need more
+ *   scratch than the array holds (moe_workspace_bytes(MOE_OP_ROUTE, ...) gives
+ *   the need for bf16 x); other checks as moe_route.
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind (the pass needs no cleared scratch): calls that overlap on one GPU
+ *   race, so order them on one stream.
+ */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+int moe_route_noalloc(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g,
+                      const float* b_g, const float* b_sel, int32_t E, int32_t k, const float* noise,
+                      float noise_std, float temperature, int64_t capacity, float alpha, float beta,
+                      float* logits, float* lse, int32_t* topk_idx, float* topk_gate,
+                      int32_t* expert_count, int32_t* expert_offset, int32_t* slot, int32_t* row,
+                      int32_t* row_token, float* f, float* P, float* losses, hipStream_t stream);
 
 /*
  * Grouped expert FFN over packed rows: for every group g and every row r in

@@ -30,6 +30,8 @@ SIGNATURES = {
                             _SZ, _P]),
     "moe_route": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _F32, _I64, _F32, _F32]
                   + [_P] * 12 + [_P, _SZ, _P]),
+    "moe_route_noalloc": (_INT, [_P, _INT, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _F32, _F32, _I64, _F32, _F32]
+                          + [_P] * 12 + [_P]),
     "moe_grouped_ffn": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _I32, _INT, _INT, _P, _P, _P, _P,
                                _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_up": (_INT, [_P, _P, _P, _I32, _I64, _I32, _I32, _INT, _INT, _P, _P, _P, _P, _P, _SZ,

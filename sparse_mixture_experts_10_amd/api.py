@@ -127,6 +127,18 @@ def moe_route(x, W_g, b_g, b_sel, k, capacity, alpha, beta, logits, lse, topk_id
         _p(row_token), _p(f), _p(P), _p(losses), wp, wn, _s(stream)))
 
 
+def moe_route_noalloc(x, W_g, b_g, b_sel, k, capacity, alpha, beta, logits, lse, topk_idx, topk_gate,
+                      expert_count, expert_offset, slot, row, row_token, f, P, losses, stream=None, noise=None,
+                      noise_std=0.0, temperature=1.0):
+    """moe_route with its scratch in the library's static device array (no workspace)."""
+    T, d = x.shape
+    E = W_g.shape[0]
+    _check("moe_route_noalloc", load().moe_route_noalloc(
+        _p(x), _dt(x), T, d, _p(W_g), _p(b_g), _p(b_sel), E, k, _p(noise), noise_std, temperature, capacity,
+        alpha, beta, _p(logits), _p(lse), _p(topk_idx), _p(topk_gate), _p(expert_count), _p(expert_offset),
+        _p(slot), _p(row), _p(row_token), _p(f), _p(P), _p(losses), _s(stream)))
+
+
 def moe_grouped_ffn(a, group_offset, max_rows, W1, b1, W2, b2, act, hidden, out,
                     hidden_sqnorm=None, ws=None, a_rows=None, stream=None):
     G, F, d = W1.shape

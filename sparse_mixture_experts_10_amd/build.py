@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(OUT_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "gemm_bf16_v2.hip", "combine.hip", "stats.hip", "balance.hip",
-           "calib.hip", "abi.cpp"]
+           "calib.hip", "noalloc.hip", "abi.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

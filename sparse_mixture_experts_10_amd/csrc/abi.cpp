@@ -108,6 +108,56 @@ size_t stats_ws(int64_t T, int32_t E, int32_t k, bool credit) {
 
 }  // namespace
 
+namespace moe {
+
+int route_check(const RouteCall& c, size_t* ws_need) {
+  if (int rc = check_ek(c.E, c.k)) return rc;
+  if (c.T < 0 || c.d < 1 || c.d % 8 != 0 || c.capacity < -1) return MOE_ERR_INVALID_ARG;
+  if (!temperature_ok(c.temperature)) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(c.x_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (c.T * (int64_t)c.k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!c.expert_count || !c.expert_offset) return MOE_ERR_INVALID_ARG;
+  if (c.T > 0) {
+    if (!c.x || !c.W_g || !c.logits || !c.lse || !c.topk_idx || !c.topk_gate || !c.slot || !c.row ||
+        !c.row_token || !c.f || !c.P || !c.losses)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(c.x) || !aligned16(c.W_g)) return MOE_ERR_INVALID_ARG;
+  }
+  *ws_need = route_ws(c.T, c.d, c.E, c.x_dtype == MOE_BF16);
+  return MOE_OK;
+}
+
+int route_run(const RouteCall& c, void* ws, hipStream_t stream) {
+  const int64_t T = c.T;
+  const int32_t d = c.d, E = c.E, k = c.k;
+  const bool xbf16 = c.x_dtype == MOE_BF16;
+  RouteStats rs{c.logits, c.lse, c.alpha, c.beta, c.f, c.P, c.losses};
+  if (T > 0 && route_counts_in_router(T, d, E, xbf16)) {
+    // two kernels: the counting router, then the scatter
+    const DispatchWs w = route_units_layout(ws, T, E);
+    const hipError_t e = launch_router_counting(c.x, xbf16, T, d, c.W_g, c.b_g, c.b_sel, E, k, c.logits,
+                                                c.lse, c.topk_idx, c.topk_gate, c.noise,
+                                                (double)c.noise_std, (double)c.temperature, w.group, w.part,
+                                                stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_dispatch(c.topk_idx, T, k, E, c.capacity, nullptr, 2, d, c.expert_count,
+                                      c.expert_offset, c.slot, c.row, c.row_token, nullptr, w, &rs, stream));
+  }
+  const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
+  if (T > 0) {
+    const hipError_t e = launch_router(c.x, xbf16, T, d, c.W_g, c.b_g, c.b_sel, E, k, c.logits, c.lse,
+                                       c.topk_idx, c.topk_gate, c.noise, (double)c.noise_std,
+                                       (double)c.temperature, ws, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return hip_status(launch_dispatch(c.topk_idx, T, k, E, c.capacity, nullptr, 2, d, c.expert_count,
+                                    c.expert_offset, c.slot, c.row, c.row_token, nullptr,
+                                    dispatch_ws_layout((char*)ws + rws, T, E), T > 0 ? &rs : nullptr,
+                                    stream));
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_string(int status) {
@@ -117,6 +167,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failure";
+    case MOE_ERR_SCRATCH: return "needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -249,45 +300,14 @@ int moe_route(const void* x, int x_dtype, int64_t T, int32_t d, const float* W_g
               float* logits, float* lse, int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
               int32_t* expert_offset, int32_t* slot, int32_t* row, int32_t* row_token, float* f,
               float* P, float* losses, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (int rc = check_ek(E, k)) return rc;
-  if (T < 0 || d < 1 || d % 8 != 0 || capacity < -1) return MOE_ERR_INVALID_ARG;
-  if (!temperature_ok(temperature)) return MOE_ERR_INVALID_ARG;
-  if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
-  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
-  if (!expert_count || !expert_offset) return MOE_ERR_INVALID_ARG;
-  if (T > 0) {
-    if (!x || !W_g || !logits || !lse || !topk_idx || !topk_gate || !slot || !row || !row_token ||
-        !f || !P || !losses)
-      return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(W_g)) return MOE_ERR_INVALID_ARG;
-  }
-  const bool xbf16 = x_dtype == MOE_BF16;
-  const size_t need = route_ws(T, d, E, xbf16);
+  const RouteCall c{x, x_dtype, T, d, W_g, b_g, b_sel, E, k, noise, noise_std, temperature, capacity, alpha,
+                    beta, logits, lse, topk_idx, topk_gate, expert_count, expert_offset, slot, row, row_token,
+                    f, P, losses};
+  size_t need = 0;
+  if (int rc = route_check(c, &need)) return rc;
   if (need > 0 && (ws == nullptr || ws_bytes < need || ((uintptr_t)ws % kWsAlign) != 0))
     return MOE_ERR_WORKSPACE;
-  RouteStats rs{logits, lse, alpha, beta, f, P, losses};
-  if (T > 0 && route_counts_in_router(T, d, E, xbf16)) {
-    // two kernels: the counting router, then the scatter
-    const DispatchWs w = route_units_layout(ws, T, E);
-    const hipError_t e = launch_router_counting(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse,
-                                                topk_idx, topk_gate, noise, (double)noise_std,
-                                                (double)temperature, w.group,
-                                                w.part, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
-                                      expert_offset, slot, row, row_token, nullptr, w, &rs, stream));
-  }
-  const size_t rws = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
-  if (T > 0) {
-    const hipError_t e = launch_router(x, xbf16, T, d, W_g, b_g, b_sel, E, k, logits, lse, topk_idx,
-                                       topk_gate, noise, (double)noise_std, (double)temperature, ws,
-                                       stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-  }
-  return hip_status(launch_dispatch(topk_idx, T, k, E, capacity, nullptr, 2, d, expert_count,
-                                    expert_offset, slot, row, row_token, nullptr,
-                                    dispatch_ws_layout((char*)ws + rws, T, E), T > 0 ? &rs : nullptr,
-                                    stream));
+  return route_run(c, ws, stream);
 }
 
 static int check_ffn_common(int32_t G, int64_t max_rows, int dtype) {

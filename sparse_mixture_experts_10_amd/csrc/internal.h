@@ -71,6 +71,32 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
                            void* x_disp, const DispatchWs& ws, const RouteStats* stats,
                            hipStream_t st);
 
+// The fused routing pass behind moe_route, split so that a caller can check
+// the arguments and size the scratch before it picks where the scratch comes
+// from.  Arguments as moe_route's (include/moe.h).
+struct RouteCall {
+  const void* x;
+  int x_dtype;
+  int64_t T;
+  int32_t d;
+  const float *W_g, *b_g, *b_sel;
+  int32_t E, k;
+  const float* noise;
+  float noise_std, temperature;
+  int64_t capacity;
+  float alpha, beta;
+  float *logits, *lse;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t *expert_count, *expert_offset, *slot, *row, *row_token;
+  float *f, *P, *losses;
+};
+// Checks every argument (nothing is enqueued); *ws_need receives the scratch
+// bytes the call needs.  Returns a MOE_* status.
+int route_check(const RouteCall& c, size_t* ws_need);
+// Enqueues the pass; c passed route_check and ws holds ws_need bytes, 256-byte aligned.
+int route_run(const RouteCall& c, void* ws, hipStream_t st);
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t st);     // picks the path below
 int gemm_bf16_n_tiles(const GemmArgs& a);                           // N tiles of that choice
 hipError_t launch_gemm_bf16_v1(const GemmArgs& a, hipStream_t st);  // any K % 8 == 0

@@ -274,3 +274,39 @@ def test_calibration_validation():
     assert lib.moe_calib_read(FAKE, 16, NULL, None) == INVALID
     assert lib.moe_calib_mfma(0, 10, FAKE, ctypes.byref(d), None) == INVALID
     assert lib.moe_calib_mfma(1, 10, FAKE, None, None) == INVALID
+
+
+def _route_noalloc(**kw):
+    a = dict(x=FAKE, dt=1, T=16, d=8, W=FAKE, bg=NULL, bs=NULL, E=4, k=2, cap=32, lg=FAKE, lse=FAKE,
+             idx=FAKE, g=FAKE, cnt=FAKE, off=FAKE, slot=FAKE, row=FAKE, rt=FAKE, f=FAKE, P=FAKE, L=FAKE)
+    a.update(kw)
+    return _native.load().moe_route_noalloc(a["x"], a["dt"], a["T"], a["d"], a["W"], a["bg"], a["bs"], a["E"],
+                                            a["k"], None, 0.0, a.get("tau", 1.0), a["cap"], 0.01, 1e-3, a["lg"],
+                                            a["lse"], a["idx"], a["g"], a["cnt"], a["off"], a["slot"], a["row"],
+                                            a["rt"], a["f"], a["P"], a["L"], None)
+
+
+def _noalloc_max_bytes():
+    src = open(os.path.join(INCLUDE, "moe.h")).read()
+    m = re.search(r"#define MOE_ROUTE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_route_noalloc_validation_and_limit():
+    """The no-workspace routing pass checks its arguments as moe_route does and
+    rejects, before touching the device, any call needing more scratch than
+    its static array holds."""
+    assert _route_noalloc(k=5) == INVALID
+    assert _route_noalloc(x=NULL) == INVALID
+    assert _route_noalloc(tau=0.0) == INVALID
+    assert _route_noalloc(dt=5) == UNSUPPORTED
+    cap = _noalloc_max_bytes()
+    assert cap == 64 << 20
+    # the split-weight MFMA router's partials grow with T: find sizes on both sides of the limit
+    E, d, k = 128, 4096, 8
+    need = lambda T: api.moe_workspace_bytes(api.OP_ROUTE, T=T, d=d, E=E)
+    assert need(32768) <= cap                       # the large workload fits
+    big = 65536
+    assert need(big) > cap
+    assert _route_noalloc(T=big, d=d, E=E, k=k) == -5
+    assert _native.load().moe_status_string(-5) != _native.load().moe_status_string(12345)
