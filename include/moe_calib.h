@@ -37,9 +37,9 @@ int moe_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream)
 int moe_calib_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
- * `blocks` blocks of four waves; every wave runs `iters` rounds of eight
- * independent v_mfma_f32_16x16x32_bf16 on register operands.  *flops (host)
- * receives the dense bf16 flops enqueued: blocks * 4 * iters * 8 * 16384.
+ * `blocks` blocks of four waves; every wave runs `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 on register operands.  *flops (host)
+ * receives the dense bf16 flops enqueued: blocks * 4 * iters * 4 * 32768.
  * sink: one device float, written only on an impossible result.
  */
 int moe_calib_mfma(int32_t blocks, int32_t iters, float* sink, double* flops, hipStream_t stream);

@@ -1,7 +1,7 @@
 // C ABI: argument checks, workspace sizing and kernel launches.
 // Every check runs before the first launch, so a rejected call enqueues nothing.
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 

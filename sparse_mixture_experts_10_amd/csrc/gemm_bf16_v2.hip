@@ -11,9 +11,15 @@
 //    load still fetch one row's 64 SUB contiguous bytes (SUB = 2: whole
 //    128-byte cache lines);
 //  * block tile BM x BN, WGM x WGN waves, each wave (BM/WGM) x (BN/WGN) of
-//    v_mfma_f32_16x16x32_bf16 tiles; the output is staged through LDS in
-//    16 WGM-row chunks for 16-byte stores.
+//    MF x MF MFMA tiles: v_mfma_f32_32x32x16_bf16 (MF = 32) wherever the wave
+//    tile is a multiple of 32, else v_mfma_f32_16x16x32_bf16 (MF = 16).  On
+//    gfx950 the 32 x 32 form runs at the dense bf16 peak and the 16 x 16 form
+//    at about half of it (measured on MI355X with register-operand loops:
+//    2.44 against 1.41 PFLOP/s), for the same operand bytes;
+//  * the output is staged through LDS in MF WGM-row chunks for 16-byte stores.
 // Requires K % (32 SUB) == 0 (and, for S > 1, Kseg % (32 SUB) == 0).
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -22,11 +28,12 @@
 
 namespace moe {
 
-template <int BM, int BN, int WGM, int WGN, int NS, int SUB, bool SEG>
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, bool SEG, int MF>
 struct V2 {
   static constexpr int NW = WGM * WGN, NT = 64 * NW;     // waves, threads
   static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave tile
-  static constexpr int TM = WM / 16, TN = WN / 16;       // MFMA tiles per wave
+  static constexpr int TM = WM / MF, TN = WN / MF;       // MFMA tiles per wave
+  static constexpr int KQ = MF == 16 ? 1 : 2;            // MFMA k-steps per 32 of K
   static constexpr int RB = 64 * SUB;                    // bytes per stage row
   static constexpr int KS = 32 * SUB;                    // K per stage
   static constexpr int RPI = 1024 / RB;                  // rows per load instruction
@@ -37,12 +44,18 @@ struct V2 {
   static constexpr int LPW = (BM + BN + RPI * NW - 1) / (RPI * NW);
   static constexpr bool PAD = LPW * NW * RPI > BM + BN;
   static constexpr int SLAB = (BM + BN) * RB;            // bytes per stage
-  static constexpr int SR = 16 * WGM;                    // output rows staged per pass
-  static constexpr int LDC = (SR * (BN + 8) * 2 <= SLAB) ? BN + 8 : BN;  // staged row (bf16)
+  static constexpr int SR = MF * WGM;                    // output rows staged per pass
+  // staged row (bf16): padded where the SR rows then still fit one stage
+  // buffer (16 x 16 tiles), always for 32 x 32 tiles; SPLIT: the SR rows do
+  // not fit one buffer, and wave row wm's MF rows sit in stage buffer wm
+  static constexpr int LDC = (MF == 32 || SR * (BN + 8) * 2 <= SLAB) ? BN + 8 : BN;
+  static constexpr bool SPLIT = SR * LDC * 2 > SLAB;
+  static constexpr int SQ_BUF = SPLIT ? WGM : 1;         // stage buffer of the row sums of squares
+  static_assert(MF == 16 || MF == 32, "16 x 16 x 32 or 32 x 32 x 16 MFMA");
   static_assert(SUB == 1 || SUB == 2, "32- or 64-wide K stages");
-  static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "wave tiles are whole MFMA tiles");
-  static_assert(SR * LDC * 2 <= SLAB, "staged output rows must fit in one stage buffer");
-  static_assert(WGN * BM * 4 <= SLAB, "the row sums of squares live in the second stage buffer");
+  static_assert(BM % (MF * WGM) == 0 && BN % (MF * WGN) == 0, "wave tiles are whole MFMA tiles");
+  static_assert(!SPLIT || (MF * LDC * 2 <= SLAB && NS > WGM), "staged output rows must fit the stage buffers");
+  static_assert(WGN * BM * 4 <= SLAB, "the row sums of squares fit one stage buffer");
   static_assert((BM + BN) % RPI == 0, "a load instruction covers whole rows of one kind");
   static_assert(NS >= 2 && NS <= 6, "2 to 6 stages");
 };
@@ -54,12 +67,25 @@ struct V2 {
 // four SIMDs from the first, so each block can put ceil(NW / 4) waves on one
 // SIMD: the register budget is set for MINB times that many waves per SIMD
 // (six-wave blocks otherwise get a budget for three and run one block per CU).
-template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG, int ACT>
+template <int MF>
+using AccT = typename std::conditional<MF == 16, f32x4_t, f32x16_t>::type;
+
+// One MFMA: weight operand first, so each lane holds consecutive columns of
+// one output row (MF = 16: row lane % 16, columns 4 (lane / 16) + r; MF = 32:
+// row lane % 32, columns 8 (r / 4) + 4 (lane / 32) + r % 4).
+template <int MF>
+__device__ __forceinline__ void mfma_step(const bf16x8_t& w, const bf16x8_t& a, AccT<MF>& c) {
+  if constexpr (MF == 16) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, a, c, 0, 0, 0);
+  else c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, c, 0, 0, 0);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, bool SEG, int ACT, int MF>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(MINB * ((WGM * WGN + 3) / 4))))
 void gemm_bf16_v2_kernel(GemmArgs p) {
-  using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG>;
-  constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT;
+  using C = V2<BM, BN, WGM, WGN, NS, SUB, SEG, MF>;
+  constexpr int TM = C::TM, TN = C::TN, LPW = C::LPW, NW = C::NW, NT = C::NT, KQ = C::KQ;
+  using Acc = AccT<MF>;
   // ping-pong schedule (two groups of four waves, one of each a SIMD)
   constexpr bool PP = BM == 256 && BN == 256 && WGM == 2 && WGN == 4 && NS == 4 && SUB == 1;
   __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
@@ -110,7 +136,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
-    const int chunk = (lane % (4 * SUB)) ^ swz<SUB>(row);  // logical chunk stored here
+    const int chunk = (lane % (4 * SUB)) ^ swz_mf<SUB, MF>(row);  // logical chunk stored here
     if (row < BM) {
       src[i] = A + arow[i] * K + chunk * 8;
     } else {
@@ -137,45 +163,58 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     }
   };
 
-  f32x4_t acc[TM][TN];
+  Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4 * (MF / 16) * (MF / 16); ++r) acc[i][j][r] = 0.f;
 
   // operand read offsets (bytes within a stage): lane (fr, fc) reads row fr
-  // of its 16-row tile at logical k-chunk 4 h + fc of sub-slab h
-  const int fr = lane & 15, fc = lane >> 4;
+  // of its MF-row tile at logical k-chunk 4 h + fc (MF = 16) or 4 h + 2 q + fc
+  // (MF = 32, k-step q) of sub-slab h
+  const int fr = lane % MF, fc = lane / MF;
 
-  // this lane's bias columns (four bf16 per N tile; unsegmented bias), all
-  // loaded together (columns past N read column N - 4, unused): before the K
-  // loop when the register budget allows (at most four waves a SIMD), so the
-  // epilogue does not wait on them, else at the start of the epilogue
-  constexpr bool BIAS_EARLY = MINB * ((NW + 3) / 4) <= 4;
+  // this lane's bias columns (unsegmented bias), all loaded together (columns
+  // past N read column N - 4, unused): before the K loop when the register
+  // budget allows (at most four waves a SIMD, counting a wave holding more
+  // than four groups as more), so the epilogue does not wait on them, else at
+  // the start of the epilogue
+  // (MF = 16: one group of four columns per N tile; MF = 32: four groups)
+  constexpr int CG = MF == 16 ? 1 : 4;  // column groups of four a lane holds per N tile
+  constexpr bool BIAS_EARLY = MINB * ((NW + 3) / 4) * (MF == 16 ? 1 : (TN * CG + 3) / 4) <= 4;
   const bf16_t* bias = (const bf16_t*)p.bias;
-  uint2 bpre[TN];
+  uint2 bpre[TN][CG];
+  auto col_of = [&](int j, int g) { return n0 + wn * C::WN + j * MF + (MF == 16 ? fc * 4 : 8 * g + 4 * fc); };
   auto load_bias = [&]() {
     if (!SEG && bias != nullptr) {  // uniform
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * C::WN + j * 16 + fc * 4;
-        bpre[j] = *(const uint2*)(bias + (int64_t)tl.g * N + (n < N ? n : N - 4));
-      }
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+          const int n = col_of(j, g);
+          bpre[j][g] = *(const uint2*)(bias + (int64_t)tl.g * N + (n < N ? n : N - 4));
+        }
     }
   };
   if constexpr (BIAS_EARLY) load_bias();
-  int a_rd[SUB][TM], b_rd[SUB][TN];
+  int a_rd[SUB][KQ][TM], b_rd[SUB][KQ][TN];
 #pragma unroll
   for (int h = 0; h < SUB; ++h) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int R = wm * C::WM + i * 16 + fr;
-      a_rd[h][i] = R * C::RB + (((4 * h + fc) ^ swz<SUB>(R)) << 4);
-    }
+    for (int q = 0; q < KQ; ++q) {
+      const int ch = 4 * h + (MF == 16 ? fc : 2 * q + fc);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int R = BM + wn * C::WN + j * 16 + fr;
-      b_rd[h][j] = R * C::RB + (((4 * h + fc) ^ swz<SUB>(R)) << 4);
+      for (int i = 0; i < TM; ++i) {
+        const int R = wm * C::WM + i * MF + fr;
+        a_rd[h][q][i] = R * C::RB + ((ch ^ swz_mf<SUB, MF>(R)) << 4);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int R = BM + wn * C::WN + j * MF + fr;
+        b_rd[h][q][j] = R * C::RB + ((ch ^ swz_mf<SUB, MF>(R)) << 4);
+      }
     }
   }
 
@@ -195,7 +234,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     // stage j + 1 is waited for before barrier 2j + 1 (group 0) or 2j + 2
     // (group 1), ahead of both groups' reads of it.
     const int grp = wave >> 2;
-    bf16x8_t fa[TM], fb[TN];
+    bf16x8_t fa[KQ][TM], fb[KQ][TN];
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, s);
     wait_vmcnt<(NS - 2) * LPW>();  // stage 0
@@ -206,17 +245,21 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
       issue(kt + NS - 1, (stage + NS - 1) % NS);
       const char* base = stages[stage];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = *(const bf16x8_t*)(base + a_rd[0][i]);
+      for (int q = 0; q < KQ; ++q) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = *(const bf16x8_t*)(base + b_rd[0][j]);
+        for (int i = 0; i < TM; ++i) fa[q][i] = *(const bf16x8_t*)(base + a_rd[0][q][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[q][j] = *(const bf16x8_t*)(base + b_rd[0][q][j]);
+      }
       wait_vmcnt<(NS - 2) * LPW>();  // this wave's share of stage kt + 1
       slab_barrier();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int q = 0; q < KQ; ++q)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mfma_step<MF>(fb[q][j], fa[q][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       slab_barrier();
     };
@@ -239,18 +282,19 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     issue(kt + NS - 1, (stage + NS - 1) % NS);
     const char* base = stages[stage];
 #pragma unroll
-    for (int h = 0; h < SUB; ++h) {
-      bf16x8_t a[TM], b[TN];
+    for (int h = 0; h < SUB; ++h)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[h][i]);
+      for (int q = 0; q < KQ; ++q) {
+        bf16x8_t a[TM], b[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[h][j]);
+        for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[h][q][i]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[h][q][j]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mfma_step<MF>(b[j], a[i], acc[i][j]);
+      }
   };
 
   int kt = 0;
@@ -265,32 +309,35 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- epilogue: lane holds C[wm*WM + i*16 + fr][wn*WN + j*16 + 4*fc + r] ----
-  // (the weight operand goes first, so each lane holds four consecutive
-  // columns of one row; N % 8 == 0 puts all four in range or none)
+  // ---- epilogue: lane holds, for each row tile i and N tile j, row
+  // m = wm WM + i MF + fr and CG groups of four consecutive columns
+  // n = col_of(j, g) + r (the weight operand goes first; N % 8 == 0 puts all
+  // four of a group in range or none)
   if constexpr (!BIAS_EARLY) load_bias();
-  float bcol[TN][4];
-  bool ncol_ok[TN];
+  float bcol[TN][CG][4];
+  bool ncol_ok[TN][CG];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * C::WN + j * 16 + fc * 4;
-    ncol_ok[j] = n < N;
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bcol[j][r] = 0.f;
-    if (ncol_ok[j] && bias != nullptr) {
-      if (SEG) {
-        for (int q = 0; q < p.S; ++q)
+    for (int g = 0; g < CG; ++g) {
+      const int n = col_of(j, g);
+      ncol_ok[j][g] = n < N;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bcol[j][r] += bf16_to_f32(bias[(int64_t)q * N + n + r]);
-      } else {
-        const uint2 bb = bpre[j];
-        bcol[j][0] = __uint_as_float(bb.x << 16);
-        bcol[j][1] = __uint_as_float(bb.x & 0xffff0000u);
-        bcol[j][2] = __uint_as_float(bb.y << 16);
-        bcol[j][3] = __uint_as_float(bb.y & 0xffff0000u);
+      for (int r = 0; r < 4; ++r) bcol[j][g][r] = 0.f;
+      if (ncol_ok[j][g] && bias != nullptr) {
+        if (SEG) {
+          for (int q = 0; q < p.S; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bcol[j][g][r] += bf16_to_f32(bias[(int64_t)q * N + n + r]);
+        } else {
+          const uint2 bb = bpre[j][g];
+          bcol[j][g][0] = __uint_as_float(bb.x << 16);
+          bcol[j][g][1] = __uint_as_float(bb.x & 0xffff0000u);
+          bcol[j][g][2] = __uint_as_float(bb.y << 16);
+          bcol[j][g][3] = __uint_as_float(bb.y & 0xffff0000u);
+        }
       }
     }
-  }
   const bool want_sq = p.sq_part != nullptr;
   if (p.out_f32) {
     // fp32 result straight from the accumulators: 16 contiguous bytes a lane
@@ -298,52 +345,59 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int m = wm * C::WM + i * 16 + fr;
-        const int n = n0 + wn * C::WN + j * 16 + fc * 4;
-        f32x4_t v;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = act_static<ACT>(acc[i][j][r] + bcol[j][r]);
-        if (m < tl.M && ncol_ok[j]) *(f32x4_t*)(Cf + (tl.row0 + m) * (int64_t)N + n) = v;
-      }
+        for (int g = 0; g < CG; ++g) {
+          const int m = wm * C::WM + i * MF + fr;
+          const int n = col_of(j, g);
+          f32x4_t v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = act_static<ACT>(acc[i][j][4 * g + r] + bcol[j][g][r]);
+          if (m < tl.M && ncol_ok[j][g]) *(f32x4_t*)(Cf + (tl.row0 + m) * (int64_t)N + n) = v;
+        }
     return;
   }
-  bf16_t* Cs = (bf16_t*)st0;
   bf16_t* Cg = (bf16_t*)p.C;
-  float (*s_sq)[BM] = (float (*)[BM])st1;  // [WGN][BM]; the ring is idle now
-  // pass i stages row tile i of every wave row (SR rows: staging row
-  // 16 * wm + q holds tile row wm * WM + 16 i + q) and stores them
+  float (*s_sq)[BM] = (float (*)[BM])stages[C::SQ_BUF];  // [WGN][BM]; the ring is idle now
+  // Pass i stages row tile i of every wave row and stores it: staging row
+  // MF wm + q holds tile row wm WM + MF i + q, in stage buffer 0 or, split, in
+  // stage buffer wm (row q there).
+  bf16_t* Cs = C::SPLIT ? (bf16_t*)stages[wm] : (bf16_t*)st0 + wm * MF * C::LDC;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     float rs = 0.f;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      float v[4];
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[r] = act_static<ACT>(acc[i][j][r] + bcol[j][r]);
-        if (want_sq && ncol_ok[j]) rs += v[r] * v[r];
+      for (int g = 0; g < CG; ++g) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = act_static<ACT>(acc[i][j][4 * g + r] + bcol[j][g][r]);
+          if (want_sq && ncol_ok[j][g]) rs += v[r] * v[r];
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *(uint2*)(Cs + fr * C::LDC + (col_of(j, g) - n0)) = pk;
       }
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *(uint2*)(Cs + (wm * 16 + fr) * C::LDC + wn * C::WN + j * 16 + fc * 4) = pk;
-    }
     if (want_sq) {
-      // the row's 4 fc lanes, then (below) the WGN wave columns in order
-      rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
+      // the row's lanes (four for MF = 16, two for MF = 32), then (below) the
+      // WGN wave columns in order
+      if constexpr (MF == 16) rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
       rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
-      if (fc == 0) s_sq[wn][wm * C::WM + i * 16 + fr] = rs;
+      if (fc == 0) s_sq[wn][wm * C::WM + i * MF + fr] = rs;
     }
     __syncthreads();
     constexpr int VPR = BN / 8;  // 16-byte vectors per staged row
 #pragma unroll
     for (int v = tid; v < C::SR * VPR; v += NT) {
       const int sr = v / VPR, cv = v % VPR;
-      const int m = (sr >> 4) * C::WM + i * 16 + (sr & 15);
+      const int m = (sr / MF) * C::WM + i * MF + (sr % MF);
       const int n = n0 + cv * 8;
-      if (m < tl.M && n < N)
-        store16_agent(Cg + (tl.row0 + m) * (int64_t)N + n, *(const vec16*)(Cs + sr * C::LDC + cv * 8));
+      const bf16_t* row = C::SPLIT ? (const bf16_t*)stages[sr / MF] + (sr % MF) * C::LDC
+                                   : (const bf16_t*)st0 + sr * C::LDC;
+      if (m < tl.M && n < N) store16_agent(Cg + (tl.row0 + m) * (int64_t)N + n, *(const vec16*)(row + cv * 8));
     }
     __syncthreads();
   }
@@ -355,7 +409,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB>
+template <int BM, int BN, int WGM, int WGN, int NS, int SUB, int MINB, int MF>
 static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
   const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
   if (rows <= 0) return hipSuccess;
@@ -363,7 +417,7 @@ static hipError_t launch_v2(const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)grid_blocks(mt, (a.N + BN - 1) / BN));
   const dim3 block(64 * WGM * WGN);
 #define MOE_V2_LAUNCH(SEGV, ACTV) \
-  hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, SEGV, ACTV>), grid, block, 0, st, a)
+  hipLaunchKernelGGL((gemm_bf16_v2_kernel<BM, BN, WGM, WGN, NS, SUB, MINB, SEGV, ACTV, MF>), grid, block, 0, st, a)
 #define MOE_V2_BY_ACT(SEGV)                                  \
   switch (a.act) {                                           \
     case ACT_RELU: MOE_V2_LAUNCH(SEGV, ACT_RELU); break;     \
@@ -405,16 +459,23 @@ bool gemm_v2_wide_k(const GemmArgs& a) { return a.K % 64 == 0 && (a.S <= 1 || a.
 // Every configuration accumulates K in the same order, so all give the same
 // bits.
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
-  if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1>(a, st);
-  if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2>(a, st);
+  // Every tile runs the 16 x 16 x 32 MFMA: on the expert shapes the 32 x 32 x
+  // 16 form measured slower in these loops (MI355X, 128 experts of 2048 rows
+  // at d 4096, F 1536, up pass: 256 x 256 tiles 933 against 1073 TFLOP/s,
+  // 64-wide 2-stage ring 1009, no ping-pong 986).  The 16 x 16 loops run
+  // MFMA-bound at the clock the chip holds under this load (about 1.7 GHz);
+  // the 32 x 32 ones at 2.1 GHz but starved of operands, the LDS (128 bytes a
+  // cycle) and the loads into it then setting the pace.
+  if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
+  if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2, 16>(a, st);
   if (tile == 144)
-    return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2>(a, st)
-                             : launch_v2<144, 128, 3, 2, 3, 1, 2>(a, st);
-  if (tile == 145) return launch_v2<144, 128, 3, 4, 4, 2, 1>(a, st);
-  if (tile == 257) return launch_v2<128, 256, 2, 4, 3, 1, 2>(a, st);
-  if (tile == 259) return launch_v2<128, 128, 2, 4, 4, 2, 1>(a, st);
-  if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2>(a, st);
-  return launch_v2<128, 128, 2, 4, 3, 1, 2>(a, st);
+    return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2, 16>(a, st)
+                             : launch_v2<144, 128, 3, 2, 3, 1, 2, 16>(a, st);
+  if (tile == 145) return launch_v2<144, 128, 3, 4, 4, 2, 1, 16>(a, st);
+  if (tile == 257) return launch_v2<128, 256, 2, 4, 3, 1, 2, 16>(a, st);
+  if (tile == 259) return launch_v2<128, 128, 2, 4, 4, 2, 1, 16>(a, st);
+  if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2, 16>(a, st);
+  return launch_v2<128, 128, 2, 4, 3, 1, 2, 16>(a, st);
 }
 
 }  // namespace moe

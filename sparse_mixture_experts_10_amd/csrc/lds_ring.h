@@ -28,6 +28,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int SUB>
 __device__ __forceinline__ int swz(int r) { return SUB == 1 ? (r >> 1) & 3 : r & 7; }
 
+// The same for the 32 x 32 x 16 MFMA's operand reads, where lane l reads row
+// l % 32 at logical chunk c + l / 32.  Placements measured on MI355X with one
+// block of four waves issuing ds_read_b128 back to back (LDS cycles per wave
+// read; about 7.3 is conflict-free, 128 bytes a cycle): 64-byte rows,
+// (r >> 1) & 3 takes 8.2, (r >> 3) & 3 takes 7.5; 128-byte rows, r & 7 takes
+// 8.2, (r >> 1) & 7 takes 7.5.
+template <int SUB, int MF>
+__device__ __forceinline__ int swz_mf(int r) {
+  if constexpr (MF == 16) return swz<SUB>(r);
+  else return SUB == 1 ? (r >> 3) & 3 : (r >> 1) & 7;
+}
+
 // Workgroup barrier for the slab ring.  It first waits for this wave's LDS
 // reads: the compiler may leave the reads of one slab in flight across the
 // next barrier (it places its own lgkmcnt wait at their first use), and a wave

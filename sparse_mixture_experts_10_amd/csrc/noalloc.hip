@@ -17,7 +17,7 @@
 
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "internal.h"
 
 namespace moe {
