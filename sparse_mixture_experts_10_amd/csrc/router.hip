@@ -704,7 +704,13 @@ static hipError_t launch_router_ksplit(const void* x, bool xbf16, int64_t T, int
 // ---------------------------------------------------------------------------
 constexpr double kRefineRel = 5e-5;
 
-__global__ void router_split_kernel(const float* __restrict__ Wg, int E, int d,
+
+// Row order of the 3E split rows: ew = 0, [hi; mid; lo] (row p E + e holds part
+// p of expert e); ew > 0, groups of ew experts, each group's hi, mid and lo
+// rows together (row 3 ew g + p ew + q holds part p of expert ew g + q), so
+// that a wave owning one group's 3 ew columns holds all three partials of its
+// experts.
+__global__ void router_split_kernel(const float* __restrict__ Wg, int E, int d, int ew,
                                     bf16_t* __restrict__ Ws, int32_t* __restrict__ count) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *count = 0;  // refine list, filled later on this stream
   const int64_t n = (int64_t)E * d;
@@ -715,9 +721,13 @@ __global__ void router_split_kernel(const float* __restrict__ Wg, int E, int d,
     const float r1 = w - hi;  // exact: the low 16 significand bits of w
     const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
     const float lo = r1 - mid;  // exact, at most 8 significand bits
-    Ws[i] = (bf16_t)(__float_as_uint(hi) >> 16);
-    Ws[n + i] = (bf16_t)(__float_as_uint(mid) >> 16);
-    Ws[2 * n + i] = (bf16_t)(__float_as_uint(lo) >> 16);
+    const int e = (int)(i / d);
+    const int64_t col = i - (int64_t)e * d;
+    const int64_t r0 = ew > 0 ? (int64_t)(e / ew) * 3 * ew + e % ew : e;  // row of part 0
+    const int64_t step = ew > 0 ? ew : E;                                   // rows between parts
+    Ws[r0 * d + col] = (bf16_t)(__float_as_uint(hi) >> 16);
+    Ws[(r0 + step) * d + col] = (bf16_t)(__float_as_uint(mid) >> 16);
+    Ws[(r0 + 2 * step) * d + col] = (bf16_t)(__float_as_uint(lo) >> 16);
   }
 }
 
@@ -875,59 +885,221 @@ __global__ __launch_bounds__(64 * NW) void router_mfma_kernel(
   }
 }
 
-// Exact fp64 recomputation of the listed tokens, one token per block at a time.
+// The split-weight partials and the finish in one kernel for E = EP experts
+// (EP a multiple of 64) and blocks of 128 tokens: eight waves in 2 x 4, wave
+// (wm, wn) owning tokens 64 wm .. 64 wm + 63 against the 3 EP / 4 split rows
+// of expert group wn (hi, mid, lo of experts EP / 4 wn .. EP / 4 (wn + 1) - 1,
+// in the router_split_kernel grouped order), so each lane ends with the three
+// partials of the same experts.  The K loop is the grouped GEMM's (32-wide
+// stages through a 4-stage LDS ring, the 16 x 16 x 32 MFMA, K in order, the
+// ping-pong schedule).  The fp64 logits, (hi + mid) + lo as the finish kernel
+// adds them, go through LDS (over the idle ring) to the shared per-token
+// epilogue, which lists the near-ties.  Every block reads the 3 EP split rows
+// once, and x once; no partials buffer.  (Measured on MI355X, 32768 tokens,
+// d 4096, 128 experts: 154 us against 159 us for the split GEMM alone plus
+// 39 us for the finish kernel; 64-wide stages or no ping-pong measured the
+// same.)
+template <int EP>
+struct RouterFusedCfg {
+  static constexpr int NW = 8, NT = 64 * NW, WGM = 2, WGN = 4;
+  static constexpr int RW = 128;                   // tokens a block
+  static constexpr int EW = EP / WGN;              // experts a wave column
+  static constexpr int WM = RW / WGM, WN = 3 * EW; // wave tile: 64 tokens x 3 EW split rows
+  static constexpr int TM = WM / 16, TN = WN / 16, TH = EW / 16;  // MFMA tiles; tiles per part
+  static constexpr int NR = RW + 3 * EP;           // stage rows: tokens, then split rows
+  static constexpr int SLAB = NR * 64;             // 32 bf16 of K a row
+  static constexpr int LPW = NR / (16 * NW);       // 1 KB load instructions a wave per stage
+  static constexpr int NS = 4;
+  static_assert(EP % 64 == 0, "whole 16-column tiles per part and wave");
+  static_assert(NR % (16 * NW) == 0, "stage rows split evenly over the waves");
+  static_assert(NS * SLAB >= RW * EP * 8, "the fp64 logits fit in the idle ring");
+};
+
+template <int EP>
+__global__ __launch_bounds__(512) void router_fused_kernel(
+    const bf16_t* __restrict__ x, int64_t T, int d, const bf16_t* __restrict__ Ws, int k,
+    const float* __restrict__ bg, const float* __restrict__ bsel, float* __restrict__ logits,
+    float* __restrict__ lse_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ count, int32_t* __restrict__ list, const float* __restrict__ noise,
+    double sigma, double tau) {
+  using C = RouterFusedCfg<EP>;
+  constexpr int E = EP, NW = C::NW, RW = C::RW, LPW = C::LPW, TM = C::TM, TN = C::TN, TH = C::TH;
+  constexpr int NS = C::NS, SLAB = C::SLAB;
+  __shared__ __attribute__((aligned(1024))) char ring[NS * SLAB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int64_t t0 = (int64_t)blockIdx.x * RW;
+
+  // load slots: instruction j = wave + NW i fills rows 16 j .. 16 j + 15, lane l
+  // row 16 j + l / 4 at physical chunk l % 4 (token rows past T reload row T - 1)
+  const bf16_t* src[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = 16 * (wave + NW * i) + lane / 4;
+    const int chunk = (lane % 4) ^ swz<1>(row);
+    if (row < RW) {
+      const int64_t t = t0 + row < T ? t0 + row : T - 1;
+      src[i] = x + t * d + chunk * 8;
+    } else {
+      src[i] = Ws + (int64_t)(row - RW) * d + chunk * 8;
+    }
+  }
+  const int nk = d / 32;
+  auto issue = [&](int kt, int stage) {
+    const int kk = (kt < nk ? kt : nk - 1) * 32;  // past the end: harmless reload
+    char* base = ring + stage * SLAB;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kk),
+                                       (lds_ptr_t)(base + 16 * (wave + NW * i) * 64), 16, 0, 0);
+  };
+  // operand reads: lane (fr, fc) reads row fr of a 16-row tile at logical chunk fc
+  const int fr = lane & 15, fc = lane >> 4;
+  int a_rd[TM], b_rd[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int R = wm * C::WM + i * 16 + fr;
+    a_rd[i] = R * 64 + ((fc ^ swz<1>(R)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int R = RW + wn * C::WN + j * 16 + fr;
+    b_rd[j] = R * 64 + ((fc ^ swz<1>(R)) << 4);
+  }
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Ping-pong: waves 0-3 (token half 0) and 4-7 (token half 1) put one wave
+  // of each on every SIMD; every wave runs, per stage j, MEM(j): refill stage
+  // j - 1's buffer with its share of stage j + NS - 1, read stage j, wait for
+  // its share of stage j + 1; barrier; MUL(j); barrier.  Half 1 passes one
+  // extra barrier first (half 0 one after), so one wave a SIMD multiplies
+  // while the other loads and reads.
+  const int grp = wave >> 2;
+  bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  wait_vmcnt<(NS - 2) * LPW>();  // stage 0
+  slab_barrier();
+  if (grp == 1) slab_barrier();
+  auto pp_step = [&](int kt, int stage) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + NS - 1, (stage + NS - 1) % NS);
+    const char* base = ring + stage * SLAB;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *(const bf16x8_t*)(base + a_rd[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = *(const bf16x8_t*)(base + b_rd[j]);
+    wait_vmcnt<(NS - 2) * LPW>();  // this wave's share of stage kt + 1
+    slab_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    slab_barrier();
+  };
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pp_step(kt + s, s);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (kt + s < nk) pp_step(kt + s, s);
+  if (grp == 0) slab_barrier();
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // lane (fr, fc) holds token wm WM + 16 i + fr at group columns 16 j + 4 fc + r:
+  // tiles 0 .. TH - 1 the hi part of experts EW wn + 16 j + 4 fc + r, then mid,
+  // then lo (the + 0 is the GEMM's bias add)
+  double* s_h = (double*)ring;  // [RW][E]
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TH; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double h = (double)(acc[i][j][r] + 0.f) + (double)(acc[i][TH + j][r] + 0.f) +
+                         (double)(acc[i][2 * TH + j][r] + 0.f);
+        s_h[(wm * C::WM + i * 16 + fr) * E + C::EW * wn + j * 16 + fc * 4 + r] = h;
+      }
+  __syncthreads();
+  constexpr int NXE = 16, TE = E / NXE, TPP = C::NT / NXE;  // lanes a token, experts a lane, tokens a pass
+  const int eg = tid % NXE;
+#pragma unroll 1
+  for (int p = 0; p < RW / TPP; ++p) {
+    const int tl = p * TPP + tid / NXE;
+    const int64_t t = t0 + tl;
+    double a[TE];
+#pragma unroll
+    for (int j = 0; j < TE; ++j) a[j] = s_h[tl * E + eg + NXE * j];
+    const bool near = token_epilogue<TE, NXE>(a, eg, t, t < T, E, k, bg, bsel, logits, lse_out,
+                                              topk_idx, topk_gate, noise, sigma, tau, kRefineRel);
+    if (near && t < T && eg == 0) list[atomicAdd(count, 1)] = (int32_t)t;
+  }
+}
+
 // Exact recomputation of the listed tokens, in two kernels.
-//  * dots: the work items (listed token i, slice of 16 experts) are spread over
-//    the grid; 16 lanes per expert take interleaved float4 chunks of the row
-//    (products of bf16 and fp32 are exact in fp64) with all of a pass's loads
-//    in flight, then sum over the 16 lanes in a fixed order.  h[i][e] (fp64)
-//    goes to the partials buffer, which the finish kernel has consumed.
+//  * dots: work items (8 listed tokens, 8 experts) spread over the grid; a
+//    block's thread (e, l) sums columns 4 l + 128 q of expert e for all 8
+//    tokens (products of bf16 and fp32 are exact in fp64), so each W_g row
+//    is read once for 8 tokens; the 32 lanes of an expert then add up in a
+//    fixed order.  h[i][e] (fp64) goes to the partials buffer, which no
+//    longer holds partials by then.
 //  * epilogue: one wave per listed token redoes the per-token epilogue on h.
-constexpr int kRefineF4 = 16;  // float4 chunks a lane loads per pass (1024 columns a pass)
+constexpr int kRefineTok = 8;  // listed tokens a work item
+constexpr int kRefineExp = 8;  // experts a work item (32 lanes each)
 
 __global__ __launch_bounds__(256) void router_refine_dots_kernel(
     const bf16_t* __restrict__ x, int d, const float* __restrict__ Wg, int E,
     const int32_t* __restrict__ count, const int32_t* __restrict__ list, double* __restrict__ h) {
   const int n = *count;
-  const int parts = (E + 15) / 16;
+  const int parts = (E + kRefineExp - 1) / kRefineExp;
+  const int chunks = (n + kRefineTok - 1) / kRefineTok;
   const int tid = threadIdx.x;
-  const int l = tid & 15;
-  for (int64_t w = blockIdx.x; w < (int64_t)n * parts; w += gridDim.x) {  // uniform
-    const int i = (int)(w / parts);
-    const int e = (int)(w % parts) * 16 + tid / 16;
-    const int64_t t = list[i];
-    double acc = 0.0;
+  const int l = tid & 31;
+  for (int64_t w = blockIdx.x; w < (int64_t)chunks * parts; w += gridDim.x) {  // uniform
+    const int i0 = (int)(w / parts) * kRefineTok;
+    const int e = (int)(w % parts) * kRefineExp + tid / 32;
+    const bf16_t* xr[kRefineTok];
+#pragma unroll
+    for (int u = 0; u < kRefineTok; ++u) xr[u] = x + (int64_t)list[i0 + u < n ? i0 + u : n - 1] * d;
+    double acc[kRefineTok];
+#pragma unroll
+    for (int u = 0; u < kRefineTok; ++u) acc[u] = 0.0;
     if (e < E) {
-      const bf16_t* xr = x + t * (int64_t)d;
       const float* wr = Wg + (int64_t)e * d;
-      for (int c0 = 0; c0 < d; c0 += 64 * kRefineF4) {
-        float4 wv[kRefineF4];
-        uint2 xv[kRefineF4];  // four bf16
+      for (int c = 4 * l; c < d; c += 128) {
+        const float4 wv = *(const float4*)(wr + c);
+        uint2 xv[kRefineTok];  // four bf16 a token
 #pragma unroll
-        for (int q = 0; q < kRefineF4; ++q) {
-          const int col = c0 + (q * 16 + l) * 4;
-          if (col < d) {
-            wv[q] = *(const float4*)(wr + col);
-            xv[q] = *(const uint2*)(xr + col);
-          }
-        }
+        for (int u = 0; u < kRefineTok; ++u) xv[u] = *(const uint2*)(xr[u] + c);
 #pragma unroll
-        for (int q = 0; q < kRefineF4; ++q) {
-          const int col = c0 + (q * 16 + l) * 4;
-          if (col < d) {
-            acc = fma((double)__uint_as_float(xv[q].x << 16), (double)wv[q].x, acc);
-            acc = fma((double)__uint_as_float(xv[q].x & 0xffff0000u), (double)wv[q].y, acc);
-            acc = fma((double)__uint_as_float(xv[q].y << 16), (double)wv[q].z, acc);
-            acc = fma((double)__uint_as_float(xv[q].y & 0xffff0000u), (double)wv[q].w, acc);
-          }
+        for (int u = 0; u < kRefineTok; ++u) {
+          acc[u] = fma((double)__uint_as_float(xv[u].x << 16), (double)wv.x, acc[u]);
+          acc[u] = fma((double)__uint_as_float(xv[u].x & 0xffff0000u), (double)wv.y, acc[u]);
+          acc[u] = fma((double)__uint_as_float(xv[u].y << 16), (double)wv.z, acc[u]);
+          acc[u] = fma((double)__uint_as_float(xv[u].y & 0xffff0000u), (double)wv.w, acc[u]);
         }
       }
     }
-    acc += xor_lane_d<1>(acc);
-    acc += xor_lane_d<2>(acc);
-    acc += xor_lane_d<4>(acc);
-    acc += xor_lane_d<8>(acc);
-    if (l == 0 && e < E) h[(int64_t)i * E + e] = acc;
+#pragma unroll
+    for (int u = 0; u < kRefineTok; ++u) {
+      double a = acc[u];
+      a += xor_lane_d<1>(a);
+      a += xor_lane_d<2>(a);
+      a += xor_lane_d<4>(a);
+      a += xor_lane_d<8>(a);
+      a += xor_lane_d<16>(a);
+      if (l == 0 && e < E && i0 + u < n) h[(int64_t)(i0 + u) * E + e] = a;
+    }
   }
 }
 
@@ -978,16 +1150,27 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   int32_t* list = (int32_t*)(w8 + 256);
   const int64_t n = (int64_t)E * d;
   const int64_t nb = (n + 255) / 256;
+  // 128 experts: the fused kernel over blocks of 128 tokens (every block
+  // reads the 3 MB of split rows once from L2, x once)
+  const bool fused128 = EP == 128 && E == EP;
   hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, Wg,
-                     E, d, Ws, count);
+                     E, d, fused128 ? E / 4 : 0, Ws, count);
   bool fused = false;
+  if constexpr (EP == 128) {
+    if (fused128) {
+      hipLaunchKernelGGL((router_fused_kernel<128>), dim3((unsigned)((T + 127) / 128)), dim3(512), 0, st,
+                         (const bf16_t*)x, T, d, Ws, k, bg, bsel, logits, lse, idx, gate, count, list, noise,
+                         sigma, tau);
+      fused = true;
+    }
+  }
   if constexpr (EP == 64) {
     // partials and finish in one kernel where it measured faster: 64 experts
     // and 256 or more blocks of 64 tokens (switch layer, T 16384, d 1024:
     // routing pass 48.7 -> 46.7 us).  With fewer tokens (two-wave blocks:
-    // 64 experts at T 8192, d 2048, 60.6 -> 69.5 us) or 128 experts (every
-    // block re-reads 3 MB of split weights: 264 -> 324 us at T 32768, d 4096)
-    // the GEMM and the finish kernel stay ahead.
+    // 64 experts at T 8192, d 2048, 60.6 -> 69.5 us) the GEMM and the finish
+    // kernel stay ahead.  (128 experts take router_fused_kernel above, whose
+    // blocks of 128 tokens read the split rows once per 128 tokens.)
     if (E == EP && T >= 64 * 256) {
       hipLaunchKernelGGL((router_mfma_kernel<EP, 4, 4>), dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st,
                          (const bf16_t*)x, T, d, Ws, k, bg, bsel, logits, lse, idx, gate, count, list,
@@ -1010,7 +1193,7 @@ static hipError_t launch_router_mfma(const void* x, int64_t T, int d, const floa
   // the listed tokens' exact logits go into the consumed partials buffer
   // (T E doubles <= T 3E floats)
   double* h = (double*)part;
-  hipLaunchKernelGGL(router_refine_dots_kernel, dim3(1024), dim3(256), 0, st, (const bf16_t*)x, d, Wg, E,
+  hipLaunchKernelGGL(router_refine_dots_kernel, dim3(512), dim3(256), 0, st, (const bf16_t*)x, d, Wg, E,
                      count, list, h);
   hipLaunchKernelGGL((router_refine_epilogue_kernel<EP>), dim3(256), dim3(256), 0, st, h, bg, bsel, E, k,
                      count, list, logits, lse, idx, gate, noise, sigma, tau);
