@@ -34,12 +34,14 @@ inline bool temperature_ok(float tau) { return tau > 0.f && tau <= 3.402823466e3
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// dispatch scratch: chunk counts, group counts (and statistics partials)
+// dispatch scratch: chunk counts, group counts, scanned group counts (and
+// statistics partials, last)
 size_t dispatch_ws(int64_t T, int32_t E, bool with_stats = false) {
   const int64_t nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   const int64_t ngroups = (T + kStatsTokens - 1) / kStatsTokens;
   size_t b = align_up((size_t)nchunks * (size_t)E * sizeof(int32_t)) +
-             align_up((size_t)ngroups * (size_t)E * sizeof(int32_t));
+             align_up((size_t)ngroups * (size_t)E * sizeof(int32_t)) +
+             align_up((size_t)(ngroups + 1) * (size_t)E * sizeof(int32_t));
   if (with_stats) b += align_up((size_t)ngroups * (size_t)(E + 1) * sizeof(double));
   return b;
 }
@@ -53,6 +55,8 @@ DispatchWs dispatch_ws_layout(void* ws, int64_t T, int32_t E) {
   p += align_up((size_t)nchunks * (size_t)E * sizeof(int32_t));
   w.group = (int32_t*)p;
   p += align_up((size_t)ngroups * (size_t)E * sizeof(int32_t));
+  w.bases = (int32_t*)p;
+  p += align_up((size_t)(ngroups + 1) * (size_t)E * sizeof(int32_t));
   w.part = (double*)p;
   return w;
 }
@@ -79,9 +83,13 @@ static DispatchWs route_units_layout(void* ws, int64_t T, int32_t E) {
 
 size_t route_ws(int64_t T, int32_t d, int32_t E, bool xbf16) {
   if (route_counts_in_router(T, d, E, xbf16)) {
+    // the counting router's units; sized to cover the dispatch's scratch too,
+    // as the workspace query documents
     const int64_t units = (T + kStatsSub - 1) / kStatsSub;
-    return align_up((size_t)units * (size_t)E * sizeof(int32_t)) +
-           align_up((size_t)units * (size_t)(E + 1) * sizeof(double));
+    const size_t b = align_up((size_t)units * (size_t)E * sizeof(int32_t)) +
+                     align_up((size_t)units * (size_t)(E + 1) * sizeof(double));
+    const size_t dw = dispatch_ws(T, E, true);
+    return b > dw ? b : dw;
   }
   const size_t r = router_uses_mfma(xbf16, d, E) ? align_up(router_mfma_ws_bytes(T, d, E)) : 0;
   return r + dispatch_ws(T, E, true);

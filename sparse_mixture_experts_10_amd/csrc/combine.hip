@@ -9,8 +9,8 @@
 // shared term, then one rounding of the result.
 //
 // One wavefront per token; lanes stride the row in 16-byte vectors.  Lane j < k
-// fetches (row, gate) of choice j once into LDS for the whole wave; then the
-// rows of all choices (up to 8) load together.
+// fetches (row, gate) of choice j once into LDS for the whole wave; then, for
+// up to 8 choices, every choice's row at two vectors a lane loads together.
 
 #include "common.h"
 #include "internal.h"
@@ -67,7 +67,61 @@ __global__ __launch_bounds__(256) void combine_kernel(const vec16* __restrict__ 
 #pragma unroll
     for (int j = KC - 1; j >= 0; --j) rkept = rr[j] >= 0 ? rr[j] : rkept;
   }
-  for (int64_t v = lane; v < vpr; v += 64) {
+  int64_t v0 = lane;
+  if constexpr (KC > 0) {
+    // two vectors a lane per round: every choice's row at both is loaded
+    // before the first add (2 KC loads in flight a lane)
+    for (; v0 + 64 < vpr; v0 += 128) {
+      vec16 qs[2];
+      if constexpr (SH) {
+        qs[0] = ysh[t * vpr + v0];
+        qs[1] = ysh[t * vpr + v0 + 64];
+      }
+      float acc[2][EPV];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) acc[h][u] = 0.f;
+      if (rkept >= 0) {  // uniform
+        vec16 q[2][KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+          const vec16* rp = yd + (int64_t)(rr[j] >= 0 ? rr[j] : rkept) * vpr + v0;
+          q[0][j] = rp[0];
+          q[1][j] = rp[64];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < KC; ++j) {
+            float f[EPV];
+            unpack_vec<EPV>(q[h][j], f);
+#pragma unroll
+            for (int u = 0; u < EPV; ++u) {
+              const float a = fmaf(gg[j], f[u], acc[h][u]);
+              acc[h][u] = rr[j] >= 0 ? a : acc[h][u];
+            }
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (SH) {
+          float f[EPV];
+          unpack_vec<EPV>(qs[h], f);
+#pragma unroll
+          for (int u = 0; u < EPV; ++u) acc[h][u] += f[u];
+        }
+        vec16 o;
+        if constexpr (BF16) o = pack_bf16x8(acc[h]);
+        else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o.w[u] = __float_as_uint(acc[h][u]);
+        }
+        store16_agent(y + t * vpr + v0 + 64 * h, o);
+      }
+    }
+  }
+  for (int64_t v = v0; v < vpr; v += 64) {
     vec16 qs;
     if constexpr (SH) qs = ysh[t * vpr + v];
     float acc[EPV];

@@ -88,6 +88,55 @@ __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __r
   }
 }
 
+// Exclusive prefix of the per-group counts over the groups, one expert a
+// column: bases[u][e] = sum_{u' < u} group[u'][e], and bases[nunits][e] the
+// expert's total.  A block takes 64 experts; its four waves take a quarter of
+// the groups each (sums, then the quarters' prefix, then the running bases
+// written in group order).  Integer sums: exact in any order.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ group, int nunits, int E,
+                                                            int32_t* __restrict__ bases) {
+  __shared__ int s_q[4][64];
+  const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  const int per = (nunits + 3) / 4;
+  const int u0 = q * per < nunits ? q * per : nunits;
+  const int u1 = u0 + per < nunits ? u0 + per : nunits;
+  int sum = 0;
+  if (e < E) {
+    int u = u0;
+    for (; u + 7 < u1; u += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = group[(int64_t)(u + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
+    }
+    for (; u < u1; ++u) sum += group[(int64_t)u * E + e];
+  }
+  s_q[q][el] = sum;
+  __syncthreads();
+  if (e >= E) return;
+  int run = 0;
+  for (int qq = 0; qq < q; ++qq) run += s_q[qq][el];
+  int u = u0;
+  for (; u + 7 < u1; u += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = group[(int64_t)(u + i) * E + e];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bases[(int64_t)(u + i) * E + e] = run;
+      run += v[i];
+    }
+  }
+  for (; u < u1; ++u) {
+    const int v = group[(int64_t)u * E + e];
+    bases[(int64_t)u * E + e] = run;
+    run += v;
+  }
+  if (q == 3) bases[(int64_t)nunits * E + e] = run;
+}
+
 // One block per chunk of 64 tokens (wave 0 ranks, all four waves copy rows),
 // plus one bookkeeping block (blockIdx.x == nchunks) that writes the counts and
 // offsets and, in the fused routing pass, a statistics block (nchunks + 1)
@@ -95,8 +144,8 @@ __global__ __launch_bounds__(256) void dispatch_empty_kernel(int E, int32_t* __r
 // not wait behind the statistics' loads and sums.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int64_t cap,
-    const int32_t* __restrict__ hist, const int32_t* __restrict__ group, int nunits, int unit_tokens,
-    int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ group, const int32_t* __restrict__ bases,
+    int nunits, int unit_tokens, int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot,
     int32_t* __restrict__ row, int32_t* __restrict__ row_token, const vec16* __restrict__ x,
     int64_t vecs_per_row, vec16* __restrict__ x_disp, const double* __restrict__ part, float alpha,
     float beta, float* __restrict__ f, float* __restrict__ Pm, float* __restrict__ losses) {
@@ -129,12 +178,23 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 #pragma unroll
   for (int j = 0; j < kChoicePrefetch; ++j) ch[j] = (!books && wave == 0 && t < T && j < k) ? idx[t * k + j] : 0;
 
-  // arrival base of this chunk and totals per expert from the per-unit counts
-  // (units of 256 tokens, plus the per-chunk counts inside the chunk's unit;
-  // or units of 16 tokens).  Thread (q, e) sums units q, q + Q, ...
-  // (Q = 256 / E thread rows), eight loads in flight; integer sums, so the
-  // split does not change the result.
-  {
+  // arrival base of this chunk and totals per expert: with the scanned bases,
+  // the chunk's unit base plus the per-chunk counts before it inside the unit;
+  // otherwise summed from the per-unit counts (units of 256 tokens, plus the
+  // per-chunk counts inside the chunk's unit; or units of 16 tokens), thread
+  // (q, e) summing units q, q + Q, ... (Q = 256 / E thread rows), eight loads
+  // in flight.  Integer sums, so either way gives the same result.
+  if (bases != nullptr) {  // uniform
+    if (stat_blk) stats_finish_sums(part, ngroups, E, s_red, s_z, unit_tokens == kStatsSub ? nunits : 0);
+    if (tid < E) {
+      int pre = bases[(int64_t)grp * E + tid];
+      const int tot = bases[(int64_t)nunits * E + tid];
+      if (!books && unit_tokens > kDispatchChunk)
+        for (int64_t cc = grp * kGroupChunks; cc < c; ++cc) pre += hist[cc * E + tid];
+      s_base[tid] = pre;
+      s_cnt[tid] = tot;
+    }
+  } else {
     const int Q = 256 / E;
     const int e = tid % E, q = tid / E;
     int pre = 0, tot = 0;
@@ -283,9 +343,17 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int64_t 
                        ws.hist, ws.group, stats ? stats->logits : nullptr, stats ? stats->lse : nullptr,
                        ws.part);
   }
+  // many units of counts: scan them once for every chunk block (linear in
+  // T), instead of every chunk block summing all units (which grows as T^2)
+  const int32_t* bases = nullptr;
+  if (!ws.units16 && ws.bases != nullptr && nunits * E > kScanMinCounts) {
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)((E + 63) / 64)), dim3(256), 0, st, ws.group,
+                       (int)nunits, E, ws.bases);
+    bases = ws.bases;
+  }
   const int64_t vpr = (int64_t)d * elem_bytes / 16;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((unsigned)(nchunks + (stats ? 2 : 1))), dim3(256), 0, st, idx, T, k, E,
-                     capacity, ws.hist, ws.group, (int)nunits, unit, count, offset, slot, row, row_token,
+                     capacity, ws.hist, ws.group, bases, (int)nunits, unit, count, offset, slot, row, row_token,
                      (const vec16*)x, vpr, (vec16*)x_disp, ws.part, stats ? stats->alpha : 0.f,
                      stats ? stats->beta : 0.f, stats ? stats->f : nullptr, stats ? stats->P : nullptr,
                      stats ? stats->losses : nullptr);

@@ -199,25 +199,27 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
     }
   };
   if constexpr (BIAS_EARLY) load_bias();
-  int a_rd[SUB][KQ][TM], b_rd[SUB][KQ][TN];
+  // Row tile i's offsets differ from tile 0's by the constant i MF RB: the
+  // permutation of rows R and R + MF i is the same for every placement used
+  // (the bits it takes from R lie below MF), so one base per (h, q) is kept
+  // and the tile offset folds into the read's immediate.
+  int a_rd0[SUB][KQ], b_rd0[SUB][KQ];
 #pragma unroll
   for (int h = 0; h < SUB; ++h) {
 #pragma unroll
     for (int q = 0; q < KQ; ++q) {
       const int ch = 4 * h + (MF == 16 ? fc : 2 * q + fc);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int R = wm * C::WM + i * MF + fr;
-        a_rd[h][q][i] = R * C::RB + ((ch ^ swz_mf<SUB, MF>(R)) << 4);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int R = BM + wn * C::WN + j * MF + fr;
-        b_rd[h][q][j] = R * C::RB + ((ch ^ swz_mf<SUB, MF>(R)) << 4);
-      }
+      const int Ra = wm * C::WM + fr, Rb = BM + wn * C::WN + fr;
+      a_rd0[h][q] = Ra * C::RB + ((ch ^ swz_mf<SUB, MF>(Ra)) << 4);
+      b_rd0[h][q] = Rb * C::RB + ((ch ^ swz_mf<SUB, MF>(Rb)) << 4);
     }
   }
-
+  auto a_at = [&](const char* base, int h, int q, int i) {
+    return *(const bf16x8_t*)(base + a_rd0[h][q] + i * MF * C::RB);
+  };
+  auto b_at = [&](const char* base, int h, int q, int j) {
+    return *(const bf16x8_t*)(base + b_rd0[h][q] + j * MF * C::RB);
+  };
   if constexpr (PP) {
     // Ping-pong: waves 0-3 (group 0) and 4-7 (group 1) put one wave of each
     // group on every SIMD.  Every wave runs the same loop, per stage j:
@@ -247,9 +249,9 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[q][i] = *(const bf16x8_t*)(base + a_rd[0][q][i]);
+        for (int i = 0; i < TM; ++i) fa[q][i] = a_at(base, 0, q, i);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[q][j] = *(const bf16x8_t*)(base + b_rd[0][q][j]);
+        for (int j = 0; j < TN; ++j) fb[q][j] = b_at(base, 0, q, j);
       }
       wait_vmcnt<(NS - 2) * LPW>();  // this wave's share of stage kt + 1
       slab_barrier();
@@ -287,9 +289,9 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
       for (int q = 0; q < KQ; ++q) {
         bf16x8_t a[TM], b[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(base + a_rd[h][q][i]);
+        for (int i = 0; i < TM; ++i) a[i] = a_at(base, h, q, i);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(base + b_rd[h][q][j]);
+        for (int j = 0; j < TN; ++j) b[j] = b_at(base, h, q, j);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -462,10 +464,11 @@ hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   // Every tile runs the 16 x 16 x 32 MFMA: on the expert shapes the 32 x 32 x
   // 16 form measured slower in these loops (MI355X, 128 experts of 2048 rows
   // at d 4096, F 1536, up pass: 256 x 256 tiles 933 against 1073 TFLOP/s,
-  // 64-wide 2-stage ring 1009, no ping-pong 986).  The 16 x 16 loops run
-  // MFMA-bound at the clock the chip holds under this load (about 1.7 GHz);
-  // the 32 x 32 ones at 2.1 GHz but starved of operands, the LDS (128 bytes a
-  // cycle) and the loads into it then setting the pace.
+  // 64-wide 2-stage ring 1009, no ping-pong 986, ping-pong on half stages of
+  // a 2-stage 64-wide ring 667).  The 16 x 16 loops run MFMA-bound at the
+  // clock the chip holds under this load (about 1.7 GHz); the 32 x 32 ones at
+  // 2.1 GHz but starved of operands, the LDS (128 bytes a cycle) and the
+  // loads into it then setting the pace.
   if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2, 16>(a, st);
   if (tile == 144)

@@ -50,11 +50,15 @@ hipError_t launch_router_counting(const void* x, bool xbf16, int64_t T, int d, c
 // router has already written per-16-token counts into group ([ceil(T/16)][E])
 // and the statistics sub-partials into part ([ceil(T/16)][E + 1]); hist is
 // unused and no counting kernel runs.
+// bases ([ngroups + 1][E], or nullptr): the scanned group counts, used when
+// there are more than kScanMinCounts of them.
+constexpr int64_t kScanMinCounts = 4096;
 struct DispatchWs {
   int32_t* hist;
   int32_t* group;
   double* part;
   bool units16 = false;
+  int32_t* bases = nullptr;
 };
 // Routing statistics taken in the same pass as the dispatch (nullptr: none).
 struct RouteStats {

@@ -140,7 +140,18 @@ __device__ __forceinline__ void stats_finish_sums(const double* __restrict__ par
     if (has_z) z += gz;
   } else {
     if (q < Q) {
+      // groups q, q + Q, ... added in that order, sixteen stored group values
+      // (or four summed from sub-partials) loaded before they are added
       int b = q;
+      if (nsub == 0) {
+        for (; b + 15 * Q < nparts; b += 16 * Q) {
+          double v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = part[(int64_t)(b + i * Q) * C + e];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s += v[i];
+        }
+      }
       for (; b + 3 * Q < nparts; b += 4 * Q) {
         const double v0 = stats_group_value(part, b, e, C, nsub);
         const double v1 = stats_group_value(part, b + Q, e, C, nsub);

@@ -189,9 +189,12 @@ def test_edge_cases(case):
         assert (o.row.cpu().numpy()[:, 0] >= 0).sum() == o.capacity
 
 
-def test_dispatch_from_oracle_topk():
-    """Dispatch alone, fed the oracle's selection: bit-exact integers and rows."""
-    w = synth.SWITCH_ZIPF.with_(T=3000, d=64, F=8, E=64, k=2, capacity_factor=Fraction(3, 5))
+@pytest.mark.parametrize("T,E,k,cf", [(3000, 64, 2, Fraction(3, 5)), (20000, 128, 4, Fraction(9, 10))])
+def test_dispatch_from_oracle_topk(T, E, k, cf):
+    """Dispatch alone, fed the oracle's selection: bit-exact integers and rows.
+    20000 tokens x 128 experts is 79 x 128 group counts, past the point where
+    one scan of them replaces every chunk block summing them all."""
+    w = synth.SWITCH_ZIPF.with_(T=T, d=64, F=8, E=E, k=k, capacity_factor=cf)
     inp = synth.draw(w)
     ref = oracle.forward(inp, tokens=[])
     C = ref.C
