@@ -1,0 +1,474 @@
+// Persistent bf16 grouped GEMM for the large expert passes (256 x 256 tiles).
+//
+// Same contract as the other bf16 paths (C = epi(A B^T) over ragged groups,
+// see GemmArgs), for passes with several waves of 256 x 256 tiles, K a
+// multiple of 32 SUB, one K segment, bf16 output:
+//  * one block of four waves per CU, each block walking its share of the
+//    tile list (the list is dealt to the 8 XCDs in contiguous bands, as in
+//    find_tile, and inside a band to the XCD's blocks round-robin);
+//  * each wave owns a 128 x 128 output tile (8 x 8 v_mfma_f32_16x16x32_bf16
+//    tiles, 256 accumulator registers in AGPRs) and software-pipelines its
+//    K loop: while it multiplies one 32-wide step from one fragment set it
+//    reads the next step into the other and issues the global -> LDS loads
+//    (global_load_lds_dwordx4) of the stage NS ahead into the buffer the
+//    previous stage left, one barrier per stage;
+//  * between tiles, the next tile's first NS stages are issued before the
+//    finished tile's epilogue runs, so their latency hides behind it;
+//  * the epilogue is per wave: bias (staged in LDS during the tile's K
+//    loop), activation, optional row sums of squares, bf16 rows staged in
+//    a private LDS strip and written back as 16-byte stores of 256-byte row
+//    pieces, with no block barrier until the row sums are combined.  The
+//    stores are plain (write-back at the XCD's L2): they complete at L2, so
+//    the next tile's first waits, which also cover them, stay short, and the
+//    L2 writes the lines back while later tiles compute (agent-scope stores
+//    would each wait for memory).
+// The accumulation order over K is the same as every other configuration's
+// (32-wide steps in order, each one MFMA), so C is bit-identical to theirs.
+// Measured on MI355X (128 groups of 2048 rows, d 4096, F 1536): a non-
+// persistent kernel of this shape spent 20-25 % of each block in the
+// epilogue and 3-8 % waiting for its first stage, with every CU writing its
+// tile back at the same moment.
+
+#include "common.h"
+#include "internal.h"
+#include "gemm_tiles.h"
+#include "lds_ring.h"
+
+namespace moe {
+
+template <int SUB>
+struct PCfg {
+  static constexpr int BM = 256, BN = 256, NW = 4, NT = 256, WM = 128, WN = 128, MF = 16;
+  static constexpr int TM = WM / MF, TN = WN / MF;           // 8 x 8 MFMA tiles a wave
+  static constexpr int NS = SUB == 1 ? 4 : 2;               // stages in the LDS ring
+  static constexpr int RB = 64 * SUB, KS = 32 * SUB;        // bytes per stage row, K per stage
+  static constexpr int RPI = 1024 / RB;                     // rows per load instruction
+  static constexpr int LPW = (BM + BN) / (RPI * NW);        // load instructions per wave per stage
+  static constexpr int SLAB = (BM + BN) * RB;               // bytes per stage
+  static constexpr int EP = 2 * WN + 16;                    // staged output row pitch (bytes)
+  static constexpr int NMF = TM * TN;                       // MFMAs per 32-wide step
+  static constexpr int NRD = TM + TN;                       // operand reads per 32-wide step
+  static constexpr int kMaxG = 256;
+  static_assert((BM + BN) % (RPI * NW) == 0, "load instructions cover whole stages");
+  static_assert(NS * SLAB == 131072, "the ring takes 128 KB");
+};
+
+// One v_mfma_f32_16x16x32_bf16 with the accumulator tied to an AGPR quad.
+// Written as asm so the 256 accumulator registers stay in one register file
+// (as builtins the compiler moved them between AGPRs and VGPRs around every
+// MFMA) and keep their written order (asm volatile).  The compiler does not
+// know these are MFMAs: the wait states an MFMA result needs before another
+// instruction reads it are added by hand where the accumulators are read.
+__device__ __forceinline__ void mfma16_acc(const bf16x8_t& w, const bf16x8_t& a, f32x4_t& c) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(w), "v"(a));
+}
+
+// One accumulator element to a VGPR, read where it is used: as plain code
+// the compiler copied all 256 accumulators to VGPRs at the end of the K loop
+// and spilled the values the next tile needs (spill reloads wait for every
+// memory operation in flight, the next tile's loads included).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+template <int SUB, int ACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void gemm_bf16_persist_kernel(GemmArgs p) {
+  using C = PCfg<SUB>;
+  constexpr int NS = C::NS, LPW = C::LPW, TM = C::TM, TN = C::TN, NMF = C::NMF, NRD = C::NRD;
+  constexpr int BM = C::BM, BN = C::BN, NW = C::NW, MF = C::MF;
+  // one LDS array per stage: distinct objects let the compiler see that
+  // reading one stage does not alias the loads in flight into the others
+  __shared__ __attribute__((aligned(1024))) char st0[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st1[C::SLAB];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? C::SLAB : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
+  __shared__ __attribute__((aligned(16))) char s_epi[NW][MF * C::EP];  // per-wave output strips
+  __shared__ __attribute__((aligned(16))) bf16_t s_bias[BN];           // bias of the tile's columns
+  __shared__ float s_sq[2][BM];                                      // row sums of squares per wave column
+  __shared__ int s_pre[C::kMaxG + 1];                                // row-tile prefix over groups
+  __shared__ int s_goff[C::kMaxG + 1];                               // group row offsets
+  // ring slot s (s is a compile-time constant wherever this is called)
+  auto slot = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int N = p.N, K = p.K;
+  const int n_tiles = (N + BN - 1) / BN;
+  const int nk = K / C::KS;
+  const bf16_t* A = (const bf16_t*)p.A;
+  const bf16_t* B = (const bf16_t*)p.B;
+  const bf16_t* bias = (const bf16_t*)p.bias;
+  const bool grouped = p.group_offset != nullptr;
+  const int G = grouped ? p.G : 1;
+
+  // ---- row-tile table (wave 0): s_pre[g] = row tiles of groups before g,
+  // s_goff[g] = first row of group g
+  if (wave == 0) {
+    if (!grouped) {
+      if (lane == 0) {
+        s_pre[0] = 0;
+        s_pre[1] = (int)((p.dense_M + BM - 1) / BM);
+        s_goff[0] = 0;
+        s_goff[1] = (int)p.dense_M;
+      }
+    } else {
+      const int gpl = (G + 63) / 64;  // groups per lane (<= 4)
+      const int g0 = lane * gpl;
+      int lo[4], hi[4], local = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = g0 + q < G ? g0 + q : G - 1;
+        lo[q] = p.group_offset[g];
+        hi[q] = p.group_offset[g + 1];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < gpl && g0 + q < G) local += (hi[q] - lo[q] + BM - 1) / BM;
+      int incl = local;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_up(incl, m, 64);
+        if (lane >= m) incl += o;
+      }
+      int pre = incl - local;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = g0 + q;
+        if (q < gpl && g < G) {
+          s_pre[g] = pre;
+          s_goff[g] = lo[q];
+          pre += (hi[q] - lo[q] + BM - 1) / BM;
+          if (g == G - 1) {
+            s_pre[G] = pre;
+            s_goff[G] = hi[q];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // list positions fit 32 bits (checked by the launcher)
+  const int total_m = __builtin_amdgcn_readfirstlane(s_pre[G]);
+  const int total = total_m * n_tiles;
+  const int band = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int first = blockIdx.x / kXcds, step = gridDim.x / kXcds;
+
+  // tile of list position i of this block's band (M = 0: nothing to do
+  // there; M = -1: past the band's end)
+  auto tile_at = [&](int i) {
+    Tile tl;
+    tl.g = 0; tl.row0 = 0; tl.M = -1; tl.nt = 0;
+    const int L = xcd * band + i;
+    if (i >= band || L >= total) return tl;
+    const int mt = L / n_tiles;
+    int lo = 0, hi = G;  // s_pre[lo] <= mt < s_pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= mt) lo = mid;
+      else hi = mid;
+    }
+    const int pre = __builtin_amdgcn_readfirstlane(s_pre[lo]);
+    const int tiles = __builtin_amdgcn_readfirstlane(s_pre[lo + 1]) - pre;
+    int r = mt - pre;
+    tl.nt = L - mt * n_tiles;
+    if (p.n_major) {
+      const int l = L - pre * n_tiles;
+      tl.nt = l / tiles;
+      r = l - tl.nt * tiles;
+    }
+    const int Mg = s_goff[lo + 1] - s_goff[lo];
+    tl.g = grouped ? lo : 0;
+    tl.row0 = (int64_t)s_goff[lo] + (int64_t)r * BM;
+    tl.M = Mg - r * BM < BM ? Mg - r * BM : BM;
+    if (tl.row0 >= p.max_rows) tl.M = 0;
+    else if (tl.row0 + tl.M > p.max_rows) tl.M = (int)(p.max_rows - tl.row0);
+    // the same for every lane: keep it in scalar registers
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.M = __builtin_amdgcn_readfirstlane(tl.M);
+    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+    tl.row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)tl.row0);
+    return tl;
+  };
+
+  // ---- per-tile load slots: instruction j = wave + NW i fills stage rows
+  // RPI j .. RPI j + RPI - 1 (1 KB); lane l fills row RPI j + l / (4 SUB),
+  // physical chunk l % (4 SUB) (its logical chunk permuted by swz), so each
+  // 4 SUB lanes fetch one row's 64 SUB contiguous bytes
+  const bf16_t* src[LPW];
+  auto set_sources = [&](const Tile& tl) {
+    int64_t arow[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
+      arow[i] = tl.row0 + (row < BM ? (row < tl.M ? row : tl.M - 1) : 0);
+    }
+    if (p.a_rows != nullptr) {
+      int ai[LPW];
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) ai[i] = p.a_rows[arow[i]];
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) arow[i] = ai[i];
+    }
+    const int n0 = tl.nt * BN;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
+      const int chunk = (lane % (4 * SUB)) ^ swz_mf<SUB, MF>(row);
+      if (row < BM) {
+        src[i] = A + arow[i] * K + chunk * 8;
+      } else {
+        const int nr = row - BM;
+        const int n = (n0 + nr < N) ? n0 + nr : N - 1;
+        src[i] = B + ((int64_t)tl.g * N + n) * K + chunk * 8;
+      }
+    }
+  };
+  auto issue_one = [&](int kt, int stage, int i) {
+    const int k = (kt < nk ? kt : nk - 1) * C::KS;  // past the end: harmless reload
+    const int row0 = C::RPI * (wave + NW * i);
+    __builtin_amdgcn_global_load_lds((const void*)(src[i] + k), (lds_ptr_t)(slot(stage) + row0 * C::RB), 16, 0, 0);
+  };
+  // the tile's first NS stages
+  auto prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) issue_one(s, s, i);
+  };
+  // the tile's bias into LDS (waves 0 and 1, 64 lanes x two columns each;
+  // N % 8 == 0 keeps both columns of a lane in range or neither, and columns
+  // past N read N - 2, unused); read in the tile's epilogue
+  auto load_bias = [&](const Tile& tl) {
+    if (bias != nullptr && wave < 2) {
+      const int n = tl.nt * BN + wave * 128 + 2 * lane;
+      const bf16_t* bp = bias + (int64_t)tl.g * N + (n < N ? n : N - 2);
+      __builtin_amdgcn_global_load_lds((const void*)bp, (lds_ptr_t)(&s_bias[wave * 128]), 4, 0, 0);
+    }
+  };
+
+  // ---- operand reads: lane (fr, fc) reads row fr of its 16-row tile at
+  // logical chunk 4 h + fc of sub-slab h; tile i's offset is i 16 RB
+  const int fr = lane % MF, fc = lane / MF;
+  int a_rd0[SUB], b_rd0[SUB];
+#pragma unroll
+  for (int h = 0; h < SUB; ++h) {
+    const int ch = 4 * h + fc;
+    const int Ra = wm * C::WM + fr, Rb = BM + wn * C::WN + fr;
+    a_rd0[h] = Ra * C::RB + ((ch ^ swz_mf<SUB, MF>(Ra)) << 4);
+    b_rd0[h] = Rb * C::RB + ((ch ^ swz_mf<SUB, MF>(Rb)) << 4);
+  }
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_one = [&](int set, const char* base, int h, int r) {
+    if (r < TM) fa[set][r] = *(const bf16x8_t*)(base + a_rd0[h] + r * MF * C::RB);
+    else fb[set][r - TM] = *(const bf16x8_t*)(base + b_rd0[h] + (r - TM) * MF * C::RB);
+  };
+
+  f32x4_t acc[TM][TN];
+
+  // step h of stage kt (ring slot `stage`).  The waits count this tile's
+  // stage loads only; the previous tile's output stores, issued after this
+  // tile's first NS stages, then have to land too, which only waits longer.
+  auto sw_step = [&](int kt, int stage, int h) {
+    const int cur = SUB == 1 ? stage & 1 : h;
+    const bool last = h == SUB - 1;
+    if (last) {
+      wait_vmcnt<(NS - 2) * LPW>();  // this wave's share of stage kt + 1
+      slab_barrier();
+    }
+    const char* nbase = last ? slot((stage + 1) % NS) : slot(stage);
+    const int nh = last ? 0 : h + 1;
+    // read r after MFMA 3 NMF r / (4 NRD), load l after MFMA 1 + 3 NMF l / (4 LPW):
+    // all in the first three quarters of the step
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) {
+      mfma16_acc(fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN]);
+#pragma unroll
+      for (int r = 0; r < NRD; ++r)
+        if (3 * NMF * r / (4 * NRD) == t) read_one(cur ^ 1, nbase, nh, r);
+      if (last) {
+#pragma unroll
+        for (int l = 0; l < LPW; ++l)
+          if (1 + 3 * NMF * l / (4 * LPW) == t) issue_one(kt + NS, stage, l);
+      }
+    }
+  };
+
+  // ---- the tile loop
+  int it = first;
+  Tile tl = tile_at(it);
+  while (tl.M == 0) tl = tile_at(it += step);
+  if (tl.M < 0) return;  // uniform
+  set_sources(tl);
+  load_bias(tl);
+  prologue();
+  for (;;) {
+    // accumulators: zero, handed to the asm MFMAs through an empty asm that
+    // takes them in AGPRs, so the writes come before the wait states the
+    // first MFMA reading them needs
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+a"(acc[i][j]));
+      }
+    asm volatile("s_nop 7");
+    // stage 0 landed (at most the NS - 1 younger stages' loads in flight:
+    // the previous tile's output stores, younger still, are partly drained)
+    wait_vmcnt<(NS - 1) * LPW>();
+    slab_barrier();
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(0, slot(0), 0, r);
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) sw_step(kt + s, s, h);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (kt + s < nk) {
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) sw_step(kt + s, s, h);
+      }
+    // MFMA results need up to 18 wait states before other instructions read them
+    asm volatile("s_nop 7");
+    asm volatile("s_nop 7");
+    asm volatile("s_nop 7");
+
+    // ---- every stage load of this tile has landed and been read (and the
+    // harmless reloads past its end), and so has its bias: once every wave
+    // is here the ring is free for the next tile's first loads
+    const Tile cur_t = tl;
+    do tl = tile_at(it += step); while (tl.M == 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tl.M > 0) {
+      set_sources(tl);
+      prologue();
+    }
+
+    // ---- epilogue of cur_t: lane holds, for row tile i and column tile j,
+    // row wm 128 + 16 i + fr and columns wn 128 + 16 j + 4 fc + r
+    const int n0 = cur_t.nt * BN;
+    const bool want_sq = p.sq_part != nullptr;
+    float bc[TN][4];
+    bool ok[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = wn * C::WN + j * MF + 4 * fc;  // column within the tile
+      ok[j] = n0 + c < N;
+      if (bias != nullptr) {
+        const uint2 bb = *(const uint2*)(&s_bias[c]);
+        bc[j][0] = __uint_as_float(bb.x << 16);
+        bc[j][1] = __uint_as_float(bb.x & 0xffff0000u);
+        bc[j][2] = __uint_as_float(bb.y << 16);
+        bc[j][3] = __uint_as_float(bb.y & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bc[j][r] = 0.f;
+      }
+    }
+    char* strip = s_epi[wave];
+    // output addresses: the tile's first element (uniform) plus a 32-bit byte
+    // offset, the lane's part fixed and the row step's part uniform (64-bit
+    // per-store addresses were all formed up front and spilled, their
+    // reloads waiting for the next tile's loads)
+    char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
+    const uint32_t lane_off = (uint32_t)(((wm * C::WM + lane / 16) * N + wn * C::WN + (lane % 16) * 8) * 2);
+    // row and column checks: the lane's fixed row against a uniform bound
+    const int lane_row = wm * C::WM + lane / 16;
+    const bool col_ok = n0 + wn * C::WN + (lane % 16) * 8 < N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // one row tile at a time: kept from hoisting the next tile's
+      // accumulator reads, which would need 256 registers at once (spills,
+      // whose reloads wait for every memory operation in flight)
+      __builtin_amdgcn_sched_barrier(0);
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = act_static<ACT>(acc_read(acc[i][j][r]) + bc[j][r]);
+          if (want_sq && ok[j]) rs += v[r] * v[r];
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *(uint2*)(strip + fr * C::EP + (j * MF + 4 * fc) * 2) = pk;
+      }
+      if (want_sq) {
+        // the row's four lanes (fc), then (below) the two wave columns in order
+        rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
+        rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
+        if (fc == 0) s_sq[wn][wm * C::WM + i * MF + fr] = rs;
+      }
+      // the strip is this wave's alone: LDS keeps one wave's accesses in order
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      // 16 rows x 256 bytes: lane reads row 4 q + lane / 16, 16 bytes at lane % 16
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 4 * q + lane / 16;
+        const vec16 val = *(const vec16*)(strip + rr * C::EP + (lane % 16) * 16);
+        // formed here: the empty asm keeps the offset from being computed
+        // (and kept live) ahead of time
+        uint32_t off = lane_off;
+        asm volatile("" : "+v"(off));
+        off += (uint32_t)((i * MF + 4 * q) * N * 2);
+        if (lane_row < cur_t.M - (i * MF + 4 * q) && col_ok) *(vec16*)(cbase + off) = val;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    // every wave has read this tile's bias and row sums: the next tile's
+    // bias may land
+    __syncthreads();
+    if (want_sq)
+      for (int m = tid; m < cur_t.M; m += C::NT)
+        p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = s_sq[0][m] + s_sq[1][m];
+    if (tl.M < 0) break;  // uniform
+    load_bias(tl);
+  }
+}
+
+template <int SUB>
+static hipError_t launch_persist(const GemmArgs& a, hipStream_t st) {
+  const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
+  if (rows <= 0) return hipSuccess;
+  const int64_t mt = (rows + 255) / 256 + (a.group_offset ? a.G : 0);
+  const int64_t bound = grid_blocks(mt, (a.N + 255) / 256);
+  const int64_t blocks = bound < kCus ? bound : kCus;  // a multiple of 8 either way
+#define MOE_PERSIST(ACTV) \
+  hipLaunchKernelGGL((gemm_bf16_persist_kernel<SUB, ACTV>), dim3((unsigned)blocks), dim3(256), 0, st, a)
+  switch (a.act) {
+    case ACT_RELU: MOE_PERSIST(ACT_RELU); break;
+    case ACT_GELU: MOE_PERSIST(ACT_GELU); break;
+    case ACT_SWISH: MOE_PERSIST(ACT_SWISH); break;
+    default: MOE_PERSIST(-1); break;
+  }
+#undef MOE_PERSIST
+  return hipGetLastError();
+}
+
+bool gemm_persist_supported(const GemmArgs& a) {
+  const int64_t rows = a.group_offset ? a.max_rows : a.dense_M;
+  const int64_t list = ((rows + 255) / 256 + (a.group_offset ? a.G : 0)) * ((a.N + 255) / 256);
+  return a.S <= 1 && !a.out_f32 && a.K % 32 == 0 && a.K >= 64 && a.N % 8 == 0 &&
+         (a.group_offset == nullptr || a.G <= 256) && list < ((int64_t)1 << 30) &&
+         (int64_t)a.N * a.K < ((int64_t)1 << 31) && rows < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_bf16_persist(const GemmArgs& a, hipStream_t st) {
+  if (!gemm_persist_supported(a)) return hipErrorInvalidValue;
+  return a.K % 64 == 0 ? launch_persist<2>(a, st) : launch_persist<1>(a, st);
+}
+
+}  // namespace moe

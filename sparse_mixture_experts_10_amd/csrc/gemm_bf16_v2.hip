@@ -13,9 +13,9 @@
 //  * block tile BM x BN, WGM x WGN waves, each wave (BM/WGM) x (BN/WGN) of
 //    MF x MF MFMA tiles: v_mfma_f32_32x32x16_bf16 (MF = 32) wherever the wave
 //    tile is a multiple of 32, else v_mfma_f32_16x16x32_bf16 (MF = 16).  On
-//    gfx950 the 32 x 32 form runs at the dense bf16 peak and the 16 x 16 form
-//    at about half of it (measured on MI355X with register-operand loops:
-//    2.44 against 1.41 PFLOP/s), for the same operand bytes;
+//    gfx950 both issue at the dense bf16 rate (16 and 32 cycles: 2.29 and
+//    2.47 PFLOP/s in asm register-operand loops on MI355X), for the same
+//    operand bytes per flop at a given wave tile;
 //  * the output is staged through LDS in MF WGM-row chunks for 16-byte stores.
 // Requires K % (32 SUB) == 0 (and, for S > 1, Kseg % (32 SUB) == 0).
 
@@ -465,11 +465,13 @@ hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   // 16 form measured slower in these loops (MI355X, 128 experts of 2048 rows
   // at d 4096, F 1536, up pass: 256 x 256 tiles 933 against 1073 TFLOP/s,
   // 64-wide 2-stage ring 1009, no ping-pong 986, ping-pong on half stages of
-  // a 2-stage 64-wide ring 667).  The 16 x 16 loops run MFMA-bound at the
-  // clock the chip holds under this load (about 1.7 GHz); the 32 x 32 ones at
-  // 2.1 GHz but starved of operands, the LDS (128 bytes a cycle) and the
-  // loads into it then setting the pace.
-  if (tile == 513) return launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
+  // a 2-stage 64-wide ring 667).  Neither is bound by the matrix pipe: the
+  // waves stall on operand reads, stage loads and the per-tile epilogue.
+  // 256 x 256 tiles whose N is a multiple of 256 go to the persistent kernel
+  // (gemm_bf16_persist.hip), this one keeps the rest.
+  if (tile == 513)
+    return gemm_persist_supported(a) && a.N % 256 == 0 ? launch_gemm_bf16_persist(a, st)
+                                                        : launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2, 16>(a, st);
   if (tile == 144)
     return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2, 16>(a, st)

@@ -107,6 +107,8 @@ hipError_t launch_gemm_bf16_v1(const GemmArgs& a, hipStream_t st);  // any K % 8
 bool gemm_v2_supported(const GemmArgs& a);                         // K % 32 == 0
 bool gemm_v2_wide_k(const GemmArgs& a);                            // K % 64 == 0
 hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st);  // tile 64, 128, 144, 145, 257, 259, 256, 513
+bool gemm_persist_supported(const GemmArgs& a);                     // one K segment, bf16 out, G <= 256
+hipError_t launch_gemm_bf16_persist(const GemmArgs& a, hipStream_t st);  // persistent 256 x 256 tiles
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 hipError_t launch_sq_reduce(const float* sq_part, int n_tiles, const int32_t* group_offset, int G,
                             int64_t max_rows, float* sq, hipStream_t st);

@@ -373,6 +373,106 @@ def test_grouped_gemm_144_row_tiles(F, with_sq):
     close_out(f64(out), torch.cat(want_o).double().cpu().numpy(), "bf16", "down pass, 144-row tiles")
 
 
+
+def _torch_act(z, act):
+    if act == "gelu":
+        return 0.5 * z * (1.0 + torch.erf(z / 2.0 ** 0.5))
+    if act == "swish":
+        return z * torch.sigmoid(z)
+    if act == "relu":
+        return torch.clamp(z, min=0.0)
+    return z
+
+
+@pytest.mark.parametrize("sizes,d,F,gather,act,with_sq", [
+    ([2000, 0, 2600, 300, 3500, 1800], 768, 512, True, "gelu", True),
+    ([1650, 1540, 0, 2100, 1580, 1700, 1600, 1830], 2048, 544, False, "relu", False),
+])
+def test_grouped_gemm_persistent_tiles(sizes, d, F, gather, act, with_sq):
+    """Passes that take the persistent 256 x 256 kernel (groups of >= 1536
+    rows on average, N a multiple of 256): empty, partial and many-tile
+    groups, rows gathered through a row map, the row sums of squares, 64-wide
+    K stages (K % 64 == 0) and, for the second shape's down pass, 32-wide
+    stages (K = 544) in the N-tile-major order (N G > rows).  Every row of
+    both passes against a float32 product of the same bf16 operands, the row
+    sums of squares against the float32 activations, and two runs agree bit
+    for bit (each block walks a list of tiles; a race between one tile's
+    epilogue and the next tile's loads would show as scattered differences)."""
+    G = len(sizes)
+    off = torch.zeros(G + 1, dtype=torch.int32)
+    off[1:] = torch.cumsum(torch.tensor(sizes), 0)
+    rows = int(off[-1])
+    n_src = 5000 if gather else rows
+    say(f"[gpu] persistent grouped gemm G={G} rows={rows} d={d} F={F} gather={gather} act={act} sq={with_sq}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(n_src, d, device="cuda", generator=g).to(torch.bfloat16)
+    rmap = (torch.randint(0, n_src, (rows,), device="cuda", generator=g).to(torch.int32) if gather
+            else torch.arange(rows, dtype=torch.int32, device="cuda"))
+    W1 = (torch.randn(G, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(G, F, device="cuda", generator=g)).to(torch.bfloat16)
+    W2 = (torch.randn(G, d, F, device="cuda", generator=g) / F ** 0.5).to(torch.bfloat16)
+    b2 = (0.1 * torch.randn(G, d, device="cuda", generator=g)).to(torch.bfloat16)
+    goff = off.cuda()
+    ws = torch.empty(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=rows), dtype=torch.uint8, device="cuda")
+    runs = []
+    for _ in range(2):
+        hid = torch.zeros(rows, F, dtype=torch.bfloat16, device="cuda")
+        sq = torch.zeros(rows, dtype=torch.float32, device="cuda")
+        out = torch.zeros(rows, d, dtype=torch.bfloat16, device="cuda")
+        api.moe_expert_up(x, goff, rows, W1, b1, act, hid, sq if with_sq else None, ws if with_sq else None,
+                          a_rows=rmap if gather else None)
+        api.moe_expert_down(hid, goff, rows, W2, b2, out)
+        runs.append((hid, sq, out))
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for u, v in zip(r, runs[0]):
+            assert torch.equal(u.view(torch.int32 if u.dtype == torch.float32 else torch.int16),
+                               v.view(torch.int32 if v.dtype == torch.float32 else torch.int16))
+    hid, sq, out = runs[0]
+    want_h, want_sq, want_o = [], [], []
+    for gi in range(G):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        if r1 == r0:
+            continue
+        a = x[rmap[r0:r1].long()].float()
+        h = _torch_act(a @ W1[gi].float().t().contiguous() + b1[gi].float(), act)
+        want_h.append(h)
+        want_sq.append((h * h).sum(1))
+        want_o.append(hid[r0:r1].float() @ W2[gi].float().t().contiguous() + b2[gi].float())
+    close_out(f64(hid), torch.cat(want_h).double().cpu().numpy(), "bf16", "up pass, persistent tiles")
+    if with_sq:
+        np.testing.assert_allclose(f64(sq), torch.cat(want_sq).double().cpu().numpy(), rtol=1e-4)
+    close_out(f64(out), torch.cat(want_o).double().cpu().numpy(), "bf16", "down pass, persistent tiles")
+
+
+def test_shared_ffn_persistent_dense_tiles():
+    """One shared expert over 3000 tokens at d 768, F 1024: both dense passes
+    (no group offsets) take the persistent 256 x 256 kernel; every row against
+    a float32 product, and two runs agree bit for bit."""
+    T, d, F = 3000, 768, 1024
+    say(f"[gpu] persistent dense shared ffn T={T} d={d} F={F}")
+    g = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    W1 = (torch.randn(1, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(1, F, device="cuda", generator=g)).to(torch.bfloat16)
+    W2 = (torch.randn(1, d, F, device="cuda", generator=g) / F ** 0.5).to(torch.bfloat16)
+    b2 = (0.1 * torch.randn(1, d, device="cuda", generator=g)).to(torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        hid = torch.zeros(T, F, dtype=torch.bfloat16, device="cuda")
+        out = torch.zeros(T, d, dtype=torch.bfloat16, device="cuda")
+        api.moe_shared_ffn(x, W1, b1, W2, b2, "swish", hid, out)
+        outs.append((hid, out))
+    torch.cuda.synchronize()
+    for u, v in zip(outs[1], outs[0]):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    hid, out = outs[0]
+    want_h = _torch_act(x.float() @ W1[0].float().t().contiguous() + b1[0].float(), "swish")
+    want_o = hid.float() @ W2[0].float().t().contiguous() + b2[0].float()
+    close_out(f64(hid), want_h.double().cpu().numpy(), "bf16", "shared up, persistent dense tiles")
+    close_out(f64(out), want_o.double().cpu().numpy(), "bf16", "shared down, persistent dense tiles")
+
+
 @pytest.mark.parametrize("act", ["relu", "gelu", "swish"])
 def test_activation_accuracy(act):
     """The epilogue activations against their float64 definitions: an fp32 FFN
