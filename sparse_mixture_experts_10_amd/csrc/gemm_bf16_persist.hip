@@ -198,32 +198,37 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   // RPI j .. RPI j + RPI - 1 (1 KB); lane l fills row RPI j + l / (4 SUB),
   // physical chunk l % (4 SUB) (its logical chunk permuted by swz), so each
   // 4 SUB lanes fetch one row's 64 SUB contiguous bytes
+  // Slots i < NA hold A rows for every wave (RPI (wave + NW i) < BM), the
+  // rest weight rows: decided by i alone, at compile time.
+  constexpr int NA = LPW / 2;
+  static_assert(C::RPI * NW * NA == BM && BM == BN, "the first half of the slots loads the A rows");
   const bf16_t* src[LPW];
   auto set_sources = [&](const Tile& tl) {
-    int64_t arow[LPW];
+    int arow[NA];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
+    for (int i = 0; i < NA; ++i) {
       const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
-      arow[i] = tl.row0 + (row < BM ? (row < tl.M ? row : tl.M - 1) : 0);
+      arow[i] = (int)tl.row0 + (row < tl.M ? row : tl.M - 1);
     }
     if (p.a_rows != nullptr) {
-      int ai[LPW];
+      int ai[NA];
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) ai[i] = p.a_rows[arow[i]];
+      for (int i = 0; i < NA; ++i) ai[i] = p.a_rows[arow[i]];
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) arow[i] = ai[i];
+      for (int i = 0; i < NA; ++i) arow[i] = ai[i];
     }
     const int n0 = tl.nt * BN;
+    const bf16_t* const bt = B + (int64_t)tl.g * N * K;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int row = C::RPI * (wave + NW * i) + lane / (4 * SUB);
       const int chunk = (lane % (4 * SUB)) ^ swz_mf<SUB, MF>(row);
-      if (row < BM) {
-        src[i] = A + arow[i] * K + chunk * 8;
+      if (i < NA) {
+        src[i] = A + (int64_t)arow[i] * K + chunk * 8;
       } else {
         const int nr = row - BM;
         const int n = (n0 + nr < N) ? n0 + nr : N - 1;
-        src[i] = B + ((int64_t)tl.g * N + n) * K + chunk * 8;
+        src[i] = bt + n * K + chunk * 8;
       }
     }
   };
