@@ -47,7 +47,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 # Sources that decide which grouped-GEMM kernel runs and what it does: HBM byte
 # counters recorded for an older version of them are not reported.
-GEMM_SOURCES = ["gemm_bf16_v2.hip", "gemm_tiles.h", "grouped_gemm.hip", "gemm_args.h", "common.h", "lds_ring.h"]
+GEMM_SOURCES = ["gemm_bf16_v2.hip", "gemm_bf16_persist.hip", "gemm_tiles.h", "grouped_gemm.hip", "gemm_args.h",
+                "common.h", "lds_ring.h"]
 COUNTER_PREFIX = "traffic-json: "
 
 WORKLOADS = {
@@ -381,7 +382,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": counter_traffic(w.name),
-                 "kernel": "gemm_bf16_v2_kernel (expert up + down, 2 launches/step)",
+                 "kernel": "grouped bf16 GEMM, expert up + down (2 launches/step; gemm_bf16_persist_kernel "
+                           "on 256 x 256 tiles with N % 256 == 0, else gemm_bf16_v2_kernel)",
                  "algorithmic_bytes": g["bytes"], "algorithmic_flops": g["flops"]})
 
     line = {

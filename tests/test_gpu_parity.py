@@ -616,15 +616,20 @@ def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k, T):
     are recomputed in fp64, so the selection equals the float64 oracle's except
     where the float64 gap itself is at rounding level.  Planted: an exact
     duplicate row (exact ties: lower index wins), a row one fp32 ulp away
-    (gaps ~1e-7) and a row 1e-6 away.  E 64 at T 16411 takes the fused
-    partials-and-finish kernel (blocks of 64 tokens, the last one partial);
-    the others the split GEMM and the finish kernel."""
+    (gaps ~1e-7), a row 1e-6 away, and two more pairs of rows 1.5e-4 and
+    3e-4 apart (over unit-variance logits), whose gaps fall on both sides of
+    the refinement band (5e-5 max(1, |score|)): those just outside it are
+    ordered by the fp32 partials alone and must still match.  E 128 takes the fused 128-expert
+    kernel, E 64 at T 16411 the fused 64-expert one (blocks of 64 tokens, the
+    last one partial), the others the split GEMM and the finish kernel."""
     w = synth.LARGE_CREDIT.with_(T=T, d=d, F=32, E=E, k=k)
     inp = synth.draw(w)
     Wg = inp.W_g.copy()
     Wg[5] = Wg[3]
     Wg[7] = np.nextafter(Wg[3], np.float32(np.inf))
     Wg[9] = (Wg[3].astype(np.float64) + 1e-6 / np.sqrt(d)).astype(np.float32)
+    Wg[21] = (Wg[19].astype(np.float64) + 1.5e-4 / np.sqrt(d)).astype(np.float32)
+    Wg[23] = (Wg[22].astype(np.float64) + 3e-4 / np.sqrt(d)).astype(np.float32)
     inp.W_g = Wg
     say(f"[gpu] router mfma path E={E} d={d} k={k}")
     from synth.device import to_torch
@@ -642,8 +647,11 @@ def test_router_mfma_path_selection_is_exact_on_planted_ties(E, d, k, T):
     gap = oracle.near_tie_gap(h, k, inp.b_sel)
     got = idx.cpu().numpy()
     bad = np.nonzero((got != ref).any(axis=1))[0]
-    say(f"  tokens with gap<1e-6: {(gap < 1e-6).sum()}, mismatches: {len(bad)}")
+    rel = gap / np.maximum(1.0, np.abs(h).max(axis=1))
+    outside = ((rel > 5e-5) & (rel < 5e-4)).sum()
+    say(f"  tokens with gap<1e-6: {(gap < 1e-6).sum()}, just outside the band: {outside}, mismatches: {len(bad)}")
     assert (gap < 1e-6).sum() > 10          # the planted rows do create near-ties
+    assert outside > 5                      # and gaps just past the refinement band
     for tt in bad:
         assert gap[tt] < 1e-12, (tt, got[tt], ref[tt], gap[tt])
     close = lambda a, b, tol: np.abs(a - b) <= tol * np.maximum(1, np.abs(b))
