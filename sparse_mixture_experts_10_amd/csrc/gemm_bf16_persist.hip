@@ -93,7 +93,9 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   // ring slot s (s is a compile-time constant wherever this is called)
   auto slot = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: the load slots' LDS addresses (M0)
+  // are then scalar arithmetic, not a VGPR read back at every load
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int N = p.N, K = p.K;
   const int n_tiles = (N + BN - 1) / BN;
