@@ -104,7 +104,7 @@ void gemm_bf16_v2_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: M0 for the loads is scalar arithmetic
   const int wm = wave / WGN, wn = wave % WGN;
   const int N = p.N, K = p.K;
   const int n0 = tl.nt * BN;

@@ -792,7 +792,7 @@ __global__ __launch_bounds__(64 * NW) void router_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? SLAB : 16];
   __shared__ double s_h[RW * E];
   char* const stages[4] = {st0, st1, st2, st3};
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t0 = (int64_t)blockIdx.x * RW;
 
   // load slots: instruction j = wave + NW i fills rows 16 j .. 16 j + 15, lane l
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(512) void router_fused_kernel(
   constexpr int E = EP, NW = C::NW, RW = C::RW, LPW = C::LPW, TM = C::TM, TN = C::TN, TH = C::TH;
   constexpr int NS = C::NS, SLAB = C::SLAB;
   __shared__ __attribute__((aligned(1024))) char ring[NS * SLAB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int64_t t0 = (int64_t)blockIdx.x * RW;
 
