@@ -74,13 +74,17 @@ class MoELayer:
     MLP gate instead of W_g / b_g (always the separate calls).
     overlap_shared: run the shared experts on a side stream, concurrently with
     the routed path (forward only; calls() lists every call in order).
+    overlap_stats: run the statistics call (with credit, or after the separate
+    router and dispatch calls) on a second side stream beside the down pass
+    and the combine (forward only).
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
                  b_g=None, b_sel=None, shared: Optional[Tuple[torch.Tensor, ...]] = None,
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
                  gather_rows: bool = True, fused_route: bool = True, noise=None, noise_std: float = 0.0,
-                 temperature: float = 1.0, mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True):
+                 temperature: float = 1.0, mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True,
+                 overlap_stats: bool = True):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
@@ -91,7 +95,9 @@ class MoELayer:
         self.noise, self.noise_std = noise, float(noise_std)
         self.temperature = float(temperature)
         self.overlap_shared = overlap_shared
+        self.overlap_stats = overlap_stats
         self._side = None
+        self._side_stats = None
         self.mlp_gate = mlp_gate
         self.fused = fused_route and gather_rows and mlp_gate is None
         self.E, self.F, self.d = W1.shape
@@ -137,32 +143,60 @@ class MoELayer:
         o = self.allocate(T) if out is None else out
         if o.T != T:
             raise ValueError("output buffers were allocated for another batch size")
-        if self.shared is None or not self.overlap_shared:
-            for _, call in self.calls(x, o, stream):
+        calls = self.calls(x, o, stream)
+        names = [n for n, _ in calls]
+        side_shared = self.shared is not None and self.overlap_shared
+        side_stats = self.overlap_stats and "stats" in names and "expert_up" in names
+        if not side_shared and not side_stats:
+            for _, call in calls:
                 call()
             return o
-        # The shared experts need only x: they run on a side stream while the
-        # routed path runs, and the combine waits for them.
         main = torch.cuda.current_stream(self.device) if stream is None else stream
-        side = self._side_stream()
-        fork = torch.cuda.Event()
-        fork.record(main)
-        side.wait_event(fork)
-        self.shared_experts(x, o, side)
-        joined = torch.cuda.Event()
-        joined.record(side)
-        for name, call in self.calls(x, o, stream):
-            if name == "shared":
+        joins = []
+        if side_shared:
+            # The shared experts need only x: they run on a side stream while
+            # the routed path runs, and the combine waits for them.
+            side = self._side_stream()
+            fork = torch.cuda.Event()
+            fork.record(main)
+            side.wait_event(fork)
+            self.shared_experts(x, o, side)
+            shared_done = torch.cuda.Event()
+            shared_done.record(side)
+        for name, call in calls:
+            if name == "shared" and side_shared:
                 continue
-            if name == "combine":
-                main.wait_event(joined)
+            if name == "combine" and side_shared:
+                main.wait_event(shared_done)
+            if name == "stats" and side_stats:
+                continue
             call()
+            if name == "expert_up" and side_stats:
+                # The statistics (with credit) need the routing outputs and the
+                # up pass's ||a||^2 only, and nothing after them reads what they
+                # write: they run on a second side stream beside the down pass
+                # and the combine, and the pass ends when both are done.
+                side2 = self._stats_stream()
+                fork2 = torch.cuda.Event()
+                fork2.record(main)
+                side2.wait_event(fork2)
+                self.stats(o, side2)
+                stats_done = torch.cuda.Event()
+                stats_done.record(side2)
+                joins.append(stats_done)
+        for ev in joins:
+            main.wait_event(ev)
         return o
 
     def _side_stream(self):
         if self._side is None:
             self._side = torch.cuda.Stream(self.device)   # default priority
         return self._side
+
+    def _stats_stream(self):
+        if self._side_stats is None:
+            self._side_stats = torch.cuda.Stream(self.device)   # default priority
+        return self._side_stats
 
     def calls(self, x, o: MoEOutputs, stream=None):
         """The ABI calls of one forward pass, in order, as (name, thunk) pairs."""
