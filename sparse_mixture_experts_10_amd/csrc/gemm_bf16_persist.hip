@@ -15,13 +15,13 @@
 //  * between tiles, the next tile's first NS stages are issued before the
 //    finished tile's epilogue runs, so their latency hides behind it;
 //  * the epilogue is per wave: bias (staged in LDS during the tile's K
-//    loop), activation, optional row sums of squares, bf16 rows staged in
-//    a private LDS strip and written back as 16-byte stores of 256-byte row
-//    pieces, with no block barrier until the row sums are combined.  The
-//    stores are plain (write-back at the XCD's L2): they complete at L2, so
-//    the next tile's first waits, which also cover them, stay short, and the
-//    L2 writes the lines back while later tiles compute (agent-scope stores
-//    would each wait for memory).
+//    loop), activation, optional row sums of squares, bf16 rows written
+//    straight from registers as 16-byte stores of 64-byte row pieces (pairs
+//    of lanes exchange four columns), with no block barrier until the row
+//    sums are combined.  The stores are plain (write-back at the XCD's L2):
+//    they complete at L2, so the next tile's first waits, which also cover
+//    them, stay short, and the L2 writes the lines back while later tiles
+//    compute (agent-scope stores would each wait for memory).
 // The accumulation order over K is the same as every other configuration's
 // (32-wide steps in order, each one MFMA), so C is bit-identical to theirs.
 // Measured on MI355X (128 groups of 2048 rows, d 4096, F 1536): a non-
@@ -45,7 +45,6 @@ struct PCfg {
   static constexpr int RPI = 1024 / RB;                     // rows per load instruction
   static constexpr int LPW = (BM + BN) / (RPI * NW);        // load instructions per wave per stage
   static constexpr int SLAB = (BM + BN) * RB;               // bytes per stage
-  static constexpr int EP = 2 * WN + 16;                    // staged output row pitch (bytes)
   static constexpr int NMF = TM * TN;                       // MFMAs per 32-wide step
   static constexpr int NRD = TM + TN;                       // operand reads per 32-wide step
   static constexpr int kMaxG = 256;
@@ -85,7 +84,6 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char st1[C::SLAB];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
-  __shared__ __attribute__((aligned(16))) char s_epi[NW][MF * C::EP];  // per-wave output strips
   __shared__ __attribute__((aligned(16))) bf16_t s_bias[BN];           // bias of the tile's columns
   __shared__ float s_sq[2][BM];                                      // row sums of squares per wave column
   __shared__ int s_pre[C::kMaxG + 1];                                // row-tile prefix over groups
@@ -381,16 +379,22 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
         for (int r = 0; r < 4; ++r) bc[j][r] = 0.f;
       }
     }
-    char* strip = s_epi[wave];
-    // output addresses: the tile's first element (uniform) plus a 32-bit byte
-    // offset, the lane's part fixed and the row step's part uniform (64-bit
+    // Register-direct stores.  Lanes fc and fc ^ 1 (lane and lane ^ 16) pair
+    // up over two neighbouring column tiles 2 q, 2 q + 1: the even one keeps
+    // its four columns of tile 2 q and takes its partner's four of the same
+    // tile, the odd one takes its partner's four of tile 2 q + 1 and keeps its
+    // own, so each holds 8 consecutive columns (16 bytes) of its row: lane fc
+    // covers columns 32 q + {0, 16, 8, 24}[fc] .. + 7, the four lanes of a row
+    // 64 contiguous bytes.  No LDS round trip.
+    // Addresses: the tile's first element (uniform) plus a 32-bit byte
+    // offset, the lane's part fixed and the step's part uniform (64-bit
     // per-store addresses were all formed up front and spilled, their
-    // reloads waiting for the next tile's loads)
+    // reloads waiting for the next tile's loads); the row check is the
+    // lane's fixed row against a uniform bound.
     char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
-    const uint32_t lane_off = (uint32_t)(((wm * C::WM + lane / 16) * N + wn * C::WN + (lane % 16) * 8) * 2);
-    // row and column checks: the lane's fixed row against a uniform bound
-    const int lane_row = wm * C::WM + lane / 16;
-    const bool col_ok = n0 + wn * C::WN + (lane % 16) * 8 < N;
+    const int colbase = (fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc;
+    const uint32_t lane_off = (uint32_t)(((wm * C::WM + fr) * N + wn * C::WN + colbase) * 2);
+    const int lane_row = wm * C::WM + fr;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       // one row tile at a time: kept from hoisting the next tile's
@@ -398,6 +402,7 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
       // whose reloads wait for every memory operation in flight)
       __builtin_amdgcn_sched_barrier(0);
       float rs = 0.f;
+      uint32_t pk[TN][2];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         float v[4];
@@ -406,10 +411,8 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
           v[r] = act_static<ACT>(acc_read(acc[i][j][r]) + bc[j][r]);
           if (want_sq && ok[j]) rs += v[r] * v[r];
         }
-        uint2 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
-        *(uint2*)(strip + fr * C::EP + (j * MF + 4 * fc) * 2) = pk;
+        pk[j][0] = pack_bf16x2(v[0], v[1]);
+        pk[j][1] = pack_bf16x2(v[2], v[3]);
       }
       if (want_sq) {
         // the row's four lanes (fc), then (below) the two wave columns in order
@@ -417,23 +420,25 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
         rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
         if (fc == 0) s_sq[wn][wm * C::WM + i * MF + fr] = rs;
       }
-      // the strip is this wave's alone: LDS keeps one wave's accesses in order
-      __builtin_amdgcn_wave_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      // 16 rows x 256 bytes: lane reads row 4 q + lane / 16, 16 bytes at lane % 16
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = 4 * q + lane / 16;
-        const vec16 val = *(const vec16*)(strip + rr * C::EP + (lane % 16) * 16);
+      for (int q = 0; q < TN / 2; ++q) {
+        // permlane16_swap(X, Y) trades X's rows 1, 3 for Y's rows 0, 2 (rows
+        // of 16 lanes): even rows end with [X, partner's X], odd rows with
+        // [partner's Y, Y] -- the 8 columns each lane stores
+        const auto w0 = __builtin_amdgcn_permlane16_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
+        const auto w1 = __builtin_amdgcn_permlane16_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
+        vec16 val;
+        val.w[0] = w0[0];
+        val.w[1] = w1[0];
+        val.w[2] = w0[1];
+        val.w[3] = w1[1];
         // formed here: the empty asm keeps the offset from being computed
         // (and kept live) ahead of time
         uint32_t off = lane_off;
         asm volatile("" : "+v"(off));
-        off += (uint32_t)((i * MF + 4 * q) * N * 2);
-        if (lane_row < cur_t.M - (i * MF + 4 * q) && col_ok) *(vec16*)(cbase + off) = val;
+        off += (uint32_t)((i * MF * N + 32 * q) * 2);
+        if (lane_row < cur_t.M - i * MF && n0 + wn * C::WN + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
       }
-      __builtin_amdgcn_wave_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     // every wave has read this tile's bias and row sums: the next tile's
     // bias may land
