@@ -75,13 +75,18 @@ __device__ __forceinline__ float group_sumf(float v) {
 }
 
 // One step of the (score desc, index asc) argmax across lanes; carries x.
+// The comparisons are combined with bitwise operators and the results
+// selected, so the step is straight-line code (with the short-circuit forms
+// the compiler branched on each comparison).
 template <int M>
 __device__ __forceinline__ void argmax_step(double& s, int& e, float& x) {
   const double so = xor_lane_d<M>(s);
   const int eo = xor_lane<M>(e);
   const float xo = xor_lane_f<M>(x);
-  const bool take = (so > s) || (so == s && eo < e);
-  if (take) { s = so; e = eo; x = xo; }
+  const bool take = (so > s) | ((so == s) & (eo < e));
+  s = take ? so : s;
+  e = take ? eo : e;
+  x = take ? xo : x;
 }
 
 template <int NXE>
@@ -175,9 +180,18 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
     const bool ok = e < E;
     double hv = acc[j] + (ok ? (double)rb.g[j] : 0.0);
     if (noise != nullptr && live && ok) hv += sigma * (double)nz[j];
-    if (tau != 1.0) hv = hv / tau;  // uniform
     h[j] = ok ? hv : NEG;
-    s[j] = ok ? h[j] + (double)rb.s[j] : NEG;
+  }
+  if (tau != 1.0) {  // uniform
+    // a real branch: the empty asm keeps the fp64 divisions from being
+    // computed (and selected away) at tau = 1.  -inf / tau stays -inf.
+    asm volatile("");
+#pragma unroll
+    for (int j = 0; j < TE; ++j) h[j] = h[j] / tau;
+  }
+#pragma unroll
+  for (int j = 0; j < TE; ++j) {
+    s[j] = (eg + NXE * j < E) ? h[j] + (double)rb.s[j] : NEG;
     m = fmax(m, h[j]);
   }
   m = group_max<NXE>(m);
@@ -228,8 +242,11 @@ __device__ __forceinline__ bool token_epilogue(const double (&acc)[TE], int eg, 
 #pragma unroll
     for (int j = 0; j < TE; ++j) {
       const int e = eg + NXE * j;
-      const bool ok = (e < E) && !((taken >> j) & 1u);
-      if (ok && (s[j] > bs || (s[j] == bs && e < be))) { bs = s[j]; be = e; bx = ex[j]; }
+      const bool ok = (e < E) & (((taken >> j) & 1u) == 0u);
+      const bool take = ok & ((s[j] > bs) | ((s[j] == bs) & (e < be)));
+      bs = take ? s[j] : bs;
+      be = take ? e : be;
+      bx = take ? ex[j] : bx;
     }
     group_argmax<NXE>(bs, be, bx);
     if (flag_rel > 0.0) {
@@ -1031,7 +1048,11 @@ __global__ __launch_bounds__(512) void router_fused_kernel(
         s_h[(wm * C::WM + i * 16 + fr) * E + C::EW * wn + j * 16 + fc * 4 + r] = h;
       }
   __syncthreads();
-  constexpr int NXE = 16, TE = E / NXE, TPP = C::NT / NXE;  // lanes a token, experts a lane, tokens a pass
+  // 8 lanes a token (16 experts a lane): each selection round's cross-lane
+  // argmax is 3 exchange steps after 16 local comparisons, and the 128 tokens
+  // take 2 passes (16 lanes a token, 4 steps after 8 comparisons over 4
+  // passes, measured 4 us slower at 32768 tokens, d 4096)
+  constexpr int NXE = 8, TE = E / NXE, TPP = C::NT / NXE;  // lanes a token, experts a lane, tokens a pass
   const int eg = tid % NXE;
 #pragma unroll 1
   for (int p = 0; p < RW / TPP; ++p) {
