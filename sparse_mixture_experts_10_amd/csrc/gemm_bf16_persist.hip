@@ -29,6 +29,8 @@
 // epilogue and 3-8 % waiting for its first stage, with every CU writing its
 // tile back at the same moment.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "gemm_tiles.h"
@@ -85,7 +87,7 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? C::SLAB : 16];
   __shared__ __attribute__((aligned(16))) bf16_t s_bias[BN];           // bias of the tile's columns
-  __shared__ float s_sq[2][BM];                                      // row sums of squares per wave column
+  __shared__ float s_sq[NW][BM];                                     // row sums of squares per wave column
   __shared__ int s_pre[C::kMaxG + 1];                                // row-tile prefix over groups
   __shared__ int s_goff[C::kMaxG + 1];                               // group row offsets
   // ring slot s (s is a compile-time constant wherever this is called)
@@ -256,16 +258,23 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   };
 
   // ---- operand reads: lane (fr, fc) reads row fr of its 16-row tile at
-  // logical chunk 4 h + fc of sub-slab h; tile i's offset is i 16 RB
+  // logical chunk 4 h + fc of sub-slab h; tile i's offset is i 16 RB.  A
+  // tile of at most BM / 2 rows runs in half-height mode: every wave takes
+  // the A rows 0 .. WM - 1 against its own WN / 2 columns (wave tile
+  // WM x WN / 2, half the MFMAs of a full tile) instead of a WM x WN quarter
+  // of the full tile, half of which would multiply padding.
   const int fr = lane % MF, fc = lane / MF;
   int a_rd0[SUB], b_rd0[SUB];
+  auto set_reads = [&](bool half) {
+    const int Ra = (half ? 0 : wm * C::WM) + fr;
+    const int Rb = BM + (half ? wave * (C::WN / 2) : wn * C::WN) + fr;
 #pragma unroll
-  for (int h = 0; h < SUB; ++h) {
-    const int ch = 4 * h + fc;
-    const int Ra = wm * C::WM + fr, Rb = BM + wn * C::WN + fr;
-    a_rd0[h] = Ra * C::RB + ((ch ^ swz_mf<SUB, MF>(Ra)) << 4);
-    b_rd0[h] = Rb * C::RB + ((ch ^ swz_mf<SUB, MF>(Rb)) << 4);
-  }
+    for (int h = 0; h < SUB; ++h) {
+      const int ch = 4 * h + fc;
+      a_rd0[h] = Ra * C::RB + ((ch ^ swz_mf<SUB, MF>(Ra)) << 4);
+      b_rd0[h] = Rb * C::RB + ((ch ^ swz_mf<SUB, MF>(Rb)) << 4);
+    }
+  };
   bf16x8_t fa[2][TM], fb[2][TN];
   auto read_one = [&](int set, const char* base, int h, int r) {
     if (r < TM) fa[set][r] = *(const bf16x8_t*)(base + a_rd0[h] + r * MF * C::RB);
@@ -277,7 +286,11 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   // step h of stage kt (ring slot `stage`).  The waits count this tile's
   // stage loads only; the previous tile's output stores, issued after this
   // tile's first NS stages, then have to land too, which only waits longer.
-  auto sw_step = [&](int kt, int stage, int h) {
+  // half_c: std::true_type for the half-height mode (TN / 2 column tiles).
+  // Both modes issue the same loads.
+  auto sw_step = [&](auto half_c, int kt, int stage, int h) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int TNe = HALF ? TN / 2 : TN, NMFe = TM * TNe, NRDe = TM + TNe;
     const int cur = SUB == 1 ? stage & 1 : h;
     const bool last = h == SUB - 1;
     if (last) {
@@ -289,16 +302,56 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     // read r after MFMA 3 NMF r / (4 NRD), load l after MFMA 1 + 3 NMF l / (4 LPW):
     // all in the first three quarters of the step
 #pragma unroll
-    for (int t = 0; t < NMF; ++t) {
-      mfma16_acc(fb[cur][t % TN], fa[cur][t / TN], acc[t / TN][t % TN]);
+    for (int t = 0; t < NMFe; ++t) {
+      mfma16_acc(fb[cur][t % TNe], fa[cur][t / TNe], acc[t / TNe][t % TNe]);
 #pragma unroll
-      for (int r = 0; r < NRD; ++r)
-        if (3 * NMF * r / (4 * NRD) == t) read_one(cur ^ 1, nbase, nh, r);
+      for (int r = 0; r < NRDe; ++r)
+        if (3 * NMFe * r / (4 * NRDe) == t) read_one(cur ^ 1, nbase, nh, r);
       if (last) {
 #pragma unroll
         for (int l = 0; l < LPW; ++l)
-          if (1 + 3 * NMF * l / (4 * LPW) == t) issue_one(kt + NS, stage, l);
+          if (1 + 3 * NMFe * l / (4 * LPW) == t) issue_one(kt + NS, stage, l);
       }
+    }
+  };
+  // the tile's K loop from its stage 0 (landed and past the barrier).  The
+  // accumulators are zeroed here and handed to the asm MFMAs through an
+  // empty asm that takes them in AGPRs, so the writes come before the wait
+  // states the first MFMA reading them needs; in half-height mode the unused
+  // ones pass through an empty asm too, so both modes leave every
+  // accumulator in an AGPR (otherwise the compiler kept the untouched ones
+  // elsewhere and spilled).
+  auto k_loop = [&](auto half_c) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int NRDe = TM + (HALF ? TN / 2 : TN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+a"(acc[i][j]));
+      }
+    asm volatile("s_nop 7");
+#pragma unroll
+    for (int r = 0; r < NRDe; ++r) read_one(0, slot(0), 0, r);
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) sw_step(half_c, kt + s, s, h);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (kt + s < nk) {
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) sw_step(half_c, kt + s, s, h);
+      }
+    if constexpr (HALF) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = TN / 2; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
     }
   };
 
@@ -311,36 +364,14 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   load_bias(tl);
   prologue();
   for (;;) {
-    // accumulators: zero, handed to the asm MFMAs through an empty asm that
-    // takes them in AGPRs, so the writes come before the wait states the
-    // first MFMA reading them needs
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        asm volatile("" : "+a"(acc[i][j]));
-      }
-    asm volatile("s_nop 7");
     // stage 0 landed (at most the NS - 1 younger stages' loads in flight:
     // the previous tile's output stores, younger still, are partly drained)
     wait_vmcnt<(NS - 1) * LPW>();
     slab_barrier();
-#pragma unroll
-    for (int r = 0; r < NRD; ++r) read_one(0, slot(0), 0, r);
-    int kt = 0;
-    for (; kt + NS <= nk; kt += NS) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int h = 0; h < SUB; ++h) sw_step(kt + s, s, h);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (kt + s < nk) {
-#pragma unroll
-        for (int h = 0; h < SUB; ++h) sw_step(kt + s, s, h);
-      }
+    const bool half = tl.M <= BM / 2;  // uniform
+    set_reads(half);
+    if (half) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
     // MFMA results need up to 18 wait states before other instructions read them
     asm volatile("s_nop 7");
     asm volatile("s_nop 7");
@@ -359,93 +390,116 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     }
 
     // ---- epilogue of cur_t: lane holds, for row tile i and column tile j,
-    // row wm 128 + 16 i + fr and columns wn 128 + 16 j + 4 fc + r
+    // row wme 128 + 16 i + fr and columns wne WNe + 16 j + 4 fc + r (full
+    // tiles: wave (wm, wn), WNe = 128; half-height: wave (0, wave), WNe = 64)
     const int n0 = cur_t.nt * BN;
     const bool want_sq = p.sq_part != nullptr;
-    float bc[TN][4];
-    bool ok[TN];
+    auto epilogue = [&](auto half_c) {
+      constexpr bool HALF = decltype(half_c)::value;
+      constexpr int TNe = HALF ? TN / 2 : TN, WNe = HALF ? C::WN / 2 : C::WN;
+      const int wme = HALF ? 0 : wm, wne = HALF ? wave : wn;
+      float bc[TNe][4];
+      bool ok[TNe];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int c = wn * C::WN + j * MF + 4 * fc;  // column within the tile
-      ok[j] = n0 + c < N;
-      if (bias != nullptr) {
-        const uint2 bb = *(const uint2*)(&s_bias[c]);
-        bc[j][0] = __uint_as_float(bb.x << 16);
-        bc[j][1] = __uint_as_float(bb.x & 0xffff0000u);
-        bc[j][2] = __uint_as_float(bb.y << 16);
-        bc[j][3] = __uint_as_float(bb.y & 0xffff0000u);
-      } else {
+      for (int j = 0; j < TNe; ++j) {
+        const int c = wne * WNe + j * MF + 4 * fc;  // column within the tile
+        ok[j] = n0 + c < N;
+        if (bias != nullptr) {
+          const uint2 bb = *(const uint2*)(&s_bias[c]);
+          bc[j][0] = __uint_as_float(bb.x << 16);
+          bc[j][1] = __uint_as_float(bb.x & 0xffff0000u);
+          bc[j][2] = __uint_as_float(bb.y << 16);
+          bc[j][3] = __uint_as_float(bb.y & 0xffff0000u);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bc[j][r] = 0.f;
-      }
-    }
-    // Register-direct stores.  Lanes fc and fc ^ 1 (lane and lane ^ 16) pair
-    // up over two neighbouring column tiles 2 q, 2 q + 1: the even one keeps
-    // its four columns of tile 2 q and takes its partner's four of the same
-    // tile, the odd one takes its partner's four of tile 2 q + 1 and keeps its
-    // own, so each holds 8 consecutive columns (16 bytes) of its row: lane fc
-    // covers columns 32 q + {0, 16, 8, 24}[fc] .. + 7, the four lanes of a row
-    // 64 contiguous bytes.  No LDS round trip.
-    // Addresses: the tile's first element (uniform) plus a 32-bit byte
-    // offset, the lane's part fixed and the step's part uniform (64-bit
-    // per-store addresses were all formed up front and spilled, their
-    // reloads waiting for the next tile's loads); the row check is the
-    // lane's fixed row against a uniform bound.
-    char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
-    const int colbase = (fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc;
-    const uint32_t lane_off = (uint32_t)(((wm * C::WM + fr) * N + wn * C::WN + colbase) * 2);
-    const int lane_row = wm * C::WM + fr;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      // one row tile at a time: kept from hoisting the next tile's
-      // accumulator reads, which would need 256 registers at once (spills,
-      // whose reloads wait for every memory operation in flight)
-      __builtin_amdgcn_sched_barrier(0);
-      float rs = 0.f;
-      uint32_t pk[TN][2];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = act_static<ACT>(acc_read(acc[i][j][r]) + bc[j][r]);
-          if (want_sq && ok[j]) rs += v[r] * v[r];
+          for (int r = 0; r < 4; ++r) bc[j][r] = 0.f;
         }
-        pk[j][0] = pack_bf16x2(v[0], v[1]);
-        pk[j][1] = pack_bf16x2(v[2], v[3]);
       }
-      if (want_sq) {
-        // the row's four lanes (fc), then (below) the two wave columns in order
-        rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
-        rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
-        if (fc == 0) s_sq[wn][wm * C::WM + i * MF + fr] = rs;
-      }
+      // Register-direct stores.  Lanes fc and fc ^ 1 (lane and lane ^ 16)
+      // pair up over two neighbouring column tiles 2 q, 2 q + 1: the even one
+      // keeps its four columns of tile 2 q and takes its partner's four of
+      // the same tile, the odd one takes its partner's four of tile 2 q + 1
+      // and keeps its own, so each holds 8 consecutive columns (16 bytes) of
+      // its row: lane fc covers columns 32 q + {0, 16, 8, 24}[fc] .. + 7, the
+      // four lanes of a row 64 contiguous bytes.  No LDS round trip.
+      // Addresses: the tile's first element (uniform) plus a 32-bit byte
+      // offset, the lane's part fixed and the step's part uniform (64-bit
+      // per-store addresses were all formed up front and spilled, their
+      // reloads waiting for the next tile's loads); the row check is the
+      // lane's fixed row against a uniform bound.
+      char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
+      const int colbase = (fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc;
+      const uint32_t lane_off = (uint32_t)(((wme * C::WM + fr) * N + wne * WNe + colbase) * 2);
+      const int lane_row = wme * C::WM + fr;
 #pragma unroll
-      for (int q = 0; q < TN / 2; ++q) {
-        // permlane16_swap(X, Y) trades X's rows 1, 3 for Y's rows 0, 2 (rows
-        // of 16 lanes): even rows end with [X, partner's X], odd rows with
-        // [partner's Y, Y] -- the 8 columns each lane stores
-        const auto w0 = __builtin_amdgcn_permlane16_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
-        const auto w1 = __builtin_amdgcn_permlane16_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
-        vec16 val;
-        val.w[0] = w0[0];
-        val.w[1] = w1[0];
-        val.w[2] = w0[1];
-        val.w[3] = w1[1];
-        // formed here: the empty asm keeps the offset from being computed
-        // (and kept live) ahead of time
-        uint32_t off = lane_off;
-        asm volatile("" : "+v"(off));
-        off += (uint32_t)((i * MF * N + 32 * q) * 2);
-        if (lane_row < cur_t.M - i * MF && n0 + wn * C::WN + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
+      for (int i = 0; i < TM; ++i) {
+        // one row tile at a time: kept from hoisting the next tile's
+        // accumulator reads, which would need 256 registers at once (spills,
+        // whose reloads wait for every memory operation in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        float rs = 0.f;
+        uint32_t pk[TNe][2];
+#pragma unroll
+        for (int j = 0; j < TNe; ++j) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[r] = act_static<ACT>(acc_read(acc[i][j][r]) + bc[j][r]);
+            if (want_sq && ok[j]) rs += v[r] * v[r];
+          }
+          pk[j][0] = pack_bf16x2(v[0], v[1]);
+          pk[j][1] = pack_bf16x2(v[2], v[3]);
+        }
+        if (want_sq) {
+          // the row's four lanes (fc), then (below) the wave columns in order
+          rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
+          rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
+          if (fc == 0) s_sq[wne][wme * C::WM + i * MF + fr] = rs;
+        }
+#pragma unroll
+        for (int q = 0; q < TNe / 2; ++q) {
+          // permlane16_swap(X, Y) trades X's rows 1, 3 for Y's rows 0, 2
+          // (rows of 16 lanes): even rows end with [X, partner's X], odd rows
+          // with [partner's Y, Y] -- the 8 columns each lane stores
+          const auto w0 = __builtin_amdgcn_permlane16_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
+          const auto w1 = __builtin_amdgcn_permlane16_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
+          vec16 val;
+          val.w[0] = w0[0];
+          val.w[1] = w1[0];
+          val.w[2] = w0[1];
+          val.w[3] = w1[1];
+          // formed here: the empty asm keeps the offset from being computed
+          // (and kept live) ahead of time
+          uint32_t off = lane_off;
+          asm volatile("" : "+v"(off));
+          off += (uint32_t)((i * MF * N + 32 * q) * 2);
+          if (lane_row < cur_t.M - i * MF && n0 + wne * WNe + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
+        }
       }
+    };
+    const bool cur_half = cur_t.M <= BM / 2;  // uniform
+    if (cur_half) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
+    // every wave has read this tile's bias and written its row sums: the
+    // next tile's bias may land, the sums may be added.  LDS only, so the
+    // barrier waits for LDS accesses alone (__syncthreads would also wait
+    // for every load and store in flight: the next tile's first stages and
+    // this tile's output)
+    slab_barrier();
+    if (want_sq) {
+      // the wave columns' partial sums in column order (half-height tiles
+      // add four, so their sums round differently from a full tile's).  The
+      // empty asm keeps the row's LDS addresses from being formed at kernel
+      // start and kept (spilled) through the K loop.
+      int m0 = tid;
+      asm volatile("" : "+v"(m0));
+      if (cur_half)
+        for (int m = m0; m < cur_t.M; m += C::NT)
+          p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = ((s_sq[0][m] + s_sq[1][m]) + s_sq[2][m]) + s_sq[3][m];
+      else
+        for (int m = m0; m < cur_t.M; m += C::NT)
+          p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = s_sq[0][m] + s_sq[1][m];
     }
-    // every wave has read this tile's bias and row sums: the next tile's
-    // bias may land
-    __syncthreads();
-    if (want_sq)
-      for (int m = tid; m < cur_t.M; m += C::NT)
-        p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = s_sq[0][m] + s_sq[1][m];
     if (tl.M < 0) break;  // uniform
     load_bias(tl);
   }
