@@ -383,7 +383,7 @@ def main():
         roof = {"bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": counter_traffic(w.name),
                  "kernel": "grouped bf16 GEMM, expert up + down (2 launches/step; gemm_bf16_persist_kernel "
-                           "on 256 x 256 tiles with N % 256 == 0, else gemm_bf16_v2_kernel)",
+                           "on 256 x 256 tiles, gemm_bf16_v2_kernel on the other tile shapes)",
                  "algorithmic_bytes": g["bytes"], "algorithmic_flops": g["flops"]})
 
     line = {

@@ -258,16 +258,31 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   };
 
   // ---- operand reads: lane (fr, fc) reads row fr of its 16-row tile at
-  // logical chunk 4 h + fc of sub-slab h; tile i's offset is i 16 RB.  A
-  // tile of at most BM / 2 rows runs in half-height mode: every wave takes
-  // the A rows 0 .. WM - 1 against its own WN / 2 columns (wave tile
-  // WM x WN / 2, half the MFMAs of a full tile) instead of a WM x WN quarter
-  // of the full tile, half of which would multiply padding.
+  // logical chunk 4 h + fc of sub-slab h; tile i's offset is i 16 RB.
+  // Tile modes (M: the tile's rows, W: its columns inside N):
+  //  * full: wave (wm, wn) takes rows 128 wm .. + 127, columns 128 wn .. + 127;
+  //  * half-height (M <= 128): every wave takes rows 0 .. 127 against its
+  //    own 64 columns, 64 wave .. + 63 (wave tile 128 x 64);
+  //  * half-width (W <= 128, M > 128): every wave takes its own 64 rows,
+  //    64 wave .. + 63, against columns 0 .. 127 (wave tile 64 x 128).
+  // Either half mode has half the MFMAs of a full tile, whose other half
+  // would multiply padding.  mode_rows / mode_cols: the wave's first row and
+  // column.
+  enum { M_FULL = 0, M_HALF_H = 1, M_HALF_W = 2 };
+  // the half-width mode is built for 64-wide stages only (with the 32-wide
+  // stages' deeper ring a third K loop spilled); the others run such tiles
+  // in full mode
+  constexpr bool kHalfW = SUB == 2;
+  auto tile_mode = [&](int M, int nt) {
+    return M <= BM / 2 ? M_HALF_H : (kHalfW && N - nt * BN <= BN / 2) ? M_HALF_W : M_FULL;
+  };
+  auto mode_row = [&](int mode) { return mode == M_FULL ? wm * C::WM : mode == M_HALF_H ? 0 : wave * (C::WM / 2); };
+  auto mode_col = [&](int mode) { return mode == M_FULL ? wn * C::WN : mode == M_HALF_H ? wave * (C::WN / 2) : 0; };
   const int fr = lane % MF, fc = lane / MF;
   int a_rd0[SUB], b_rd0[SUB];
-  auto set_reads = [&](bool half) {
-    const int Ra = (half ? 0 : wm * C::WM) + fr;
-    const int Rb = BM + (half ? wave * (C::WN / 2) : wn * C::WN) + fr;
+  auto set_reads = [&](int mode) {
+    const int Ra = mode_row(mode) + fr;
+    const int Rb = BM + mode_col(mode) + fr;
 #pragma unroll
     for (int h = 0; h < SUB; ++h) {
       const int ch = 4 * h + fc;
@@ -276,9 +291,10 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     }
   };
   bf16x8_t fa[2][TM], fb[2][TN];
-  auto read_one = [&](int set, const char* base, int h, int r) {
-    if (r < TM) fa[set][r] = *(const bf16x8_t*)(base + a_rd0[h] + r * MF * C::RB);
-    else fb[set][r - TM] = *(const bf16x8_t*)(base + b_rd0[h] + (r - TM) * MF * C::RB);
+  // read r of a step: A fragments 0 .. tme - 1, then the B fragments
+  auto read_one = [&](int set, const char* base, int h, int r, int tme) {
+    if (r < tme) fa[set][r] = *(const bf16x8_t*)(base + a_rd0[h] + r * MF * C::RB);
+    else fb[set][r - tme] = *(const bf16x8_t*)(base + b_rd0[h] + (r - tme) * MF * C::RB);
   };
 
   f32x4_t acc[TM][TN];
@@ -286,11 +302,12 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   // step h of stage kt (ring slot `stage`).  The waits count this tile's
   // stage loads only; the previous tile's output stores, issued after this
   // tile's first NS stages, then have to land too, which only waits longer.
-  // half_c: std::true_type for the half-height mode (TN / 2 column tiles).
-  // Both modes issue the same loads.
-  auto sw_step = [&](auto half_c, int kt, int stage, int h) {
-    constexpr bool HALF = decltype(half_c)::value;
-    constexpr int TNe = HALF ? TN / 2 : TN, NMFe = TM * TNe, NRDe = TM + TNe;
+  // mode_c: std::integral_constant<int, mode>.  Every mode issues the same
+  // loads.
+  auto sw_step = [&](auto mode_c, int kt, int stage, int h) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int TMe = MODE == M_HALF_W ? TM / 2 : TM, TNe = MODE == M_HALF_H ? TN / 2 : TN;
+    constexpr int NMFe = TMe * TNe, NRDe = TMe + TNe;
     const int cur = SUB == 1 ? stage & 1 : h;
     const bool last = h == SUB - 1;
     if (last) {
@@ -306,7 +323,7 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
       mfma16_acc(fb[cur][t % TNe], fa[cur][t / TNe], acc[t / TNe][t % TNe]);
 #pragma unroll
       for (int r = 0; r < NRDe; ++r)
-        if (3 * NMFe * r / (4 * NRDe) == t) read_one(cur ^ 1, nbase, nh, r);
+        if (3 * NMFe * r / (4 * NRDe) == t) read_one(cur ^ 1, nbase, nh, r, TMe);
       if (last) {
 #pragma unroll
         for (int l = 0; l < LPW; ++l)
@@ -321,9 +338,10 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   // ones pass through an empty asm too, so both modes leave every
   // accumulator in an AGPR (otherwise the compiler kept the untouched ones
   // elsewhere and spilled).
-  auto k_loop = [&](auto half_c) {
-    constexpr bool HALF = decltype(half_c)::value;
-    constexpr int NRDe = TM + (HALF ? TN / 2 : TN);
+  auto k_loop = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int TMe = MODE == M_HALF_W ? TM / 2 : TM, TNe = MODE == M_HALF_H ? TN / 2 : TN;
+    constexpr int NRDe = TMe + TNe;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -333,25 +351,26 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
       }
     asm volatile("s_nop 7");
 #pragma unroll
-    for (int r = 0; r < NRDe; ++r) read_one(0, slot(0), 0, r);
+    for (int r = 0; r < NRDe; ++r) read_one(0, slot(0), 0, r, TMe);
     int kt = 0;
     for (; kt + NS <= nk; kt += NS) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int h = 0; h < SUB; ++h) sw_step(half_c, kt + s, s, h);
+        for (int h = 0; h < SUB; ++h) sw_step(mode_c, kt + s, s, h);
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       if (kt + s < nk) {
 #pragma unroll
-        for (int h = 0; h < SUB; ++h) sw_step(half_c, kt + s, s, h);
+        for (int h = 0; h < SUB; ++h) sw_step(mode_c, kt + s, s, h);
       }
-    if constexpr (HALF) {
+    if constexpr (MODE != M_FULL) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = TN / 2; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < TN; ++j)
+          if (i >= TMe || j >= TNe) asm volatile("" : "+a"(acc[i][j]));
     }
   };
 
@@ -368,10 +387,16 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     // the previous tile's output stores, younger still, are partly drained)
     wait_vmcnt<(NS - 1) * LPW>();
     slab_barrier();
-    const bool half = tl.M <= BM / 2;  // uniform
-    set_reads(half);
-    if (half) k_loop(std::true_type{});
-    else k_loop(std::false_type{});
+    // the tile's mode (uniform)
+    const int mode = tile_mode(tl.M, tl.nt);
+    set_reads(mode);
+    if (mode == M_HALF_H) {
+      k_loop(std::integral_constant<int, M_HALF_H>{});
+    } else if (mode == M_HALF_W) {
+      if constexpr (kHalfW) k_loop(std::integral_constant<int, M_HALF_W>{});
+    } else {
+      k_loop(std::integral_constant<int, M_FULL>{});
+    }
     // MFMA results need up to 18 wait states before other instructions read them
     asm volatile("s_nop 7");
     asm volatile("s_nop 7");
@@ -390,19 +415,21 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     }
 
     // ---- epilogue of cur_t: lane holds, for row tile i and column tile j,
-    // row wme 128 + 16 i + fr and columns wne WNe + 16 j + 4 fc + r (full
-    // tiles: wave (wm, wn), WNe = 128; half-height: wave (0, wave), WNe = 64)
+    // row r0 + 16 i + fr and columns c0 + 16 j + 4 fc + r, with r0, c0 the
+    // wave's first row and column in the tile's mode
     const int n0 = cur_t.nt * BN;
     const bool want_sq = p.sq_part != nullptr;
-    auto epilogue = [&](auto half_c) {
-      constexpr bool HALF = decltype(half_c)::value;
-      constexpr int TNe = HALF ? TN / 2 : TN, WNe = HALF ? C::WN / 2 : C::WN;
-      const int wme = HALF ? 0 : wm, wne = HALF ? wave : wn;
+    auto epilogue = [&](auto mode_c) {
+      constexpr int MODE = decltype(mode_c)::value;
+      constexpr int TMe = MODE == M_HALF_W ? TM / 2 : TM, TNe = MODE == M_HALF_H ? TN / 2 : TN;
+      const int r0 = mode_row(MODE), c0 = mode_col(MODE);
+      // the wave column whose row sums this wave writes
+      const int sq_col = MODE == M_FULL ? wn : MODE == M_HALF_H ? wave : 0;
       float bc[TNe][4];
       bool ok[TNe];
 #pragma unroll
       for (int j = 0; j < TNe; ++j) {
-        const int c = wne * WNe + j * MF + 4 * fc;  // column within the tile
+        const int c = c0 + j * MF + 4 * fc;  // column within the tile
         ok[j] = n0 + c < N;
         if (bias != nullptr) {
           const uint2 bb = *(const uint2*)(&s_bias[c]);
@@ -429,10 +456,10 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
       // lane's fixed row against a uniform bound.
       char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
       const int colbase = (fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc;
-      const uint32_t lane_off = (uint32_t)(((wme * C::WM + fr) * N + wne * WNe + colbase) * 2);
-      const int lane_row = wme * C::WM + fr;
+      const uint32_t lane_off = (uint32_t)(((r0 + fr) * N + c0 + colbase) * 2);
+      const int lane_row = r0 + fr;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TMe; ++i) {
         // one row tile at a time: kept from hoisting the next tile's
         // accumulator reads, which would need 256 registers at once (spills,
         // whose reloads wait for every memory operation in flight)
@@ -454,7 +481,7 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
           // the row's four lanes (fc), then (below) the wave columns in order
           rs += __int_as_float(xor_lane<16>(__float_as_int(rs)));
           rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
-          if (fc == 0) s_sq[wne][wme * C::WM + i * MF + fr] = rs;
+          if (fc == 0) s_sq[sq_col][r0 + i * MF + fr] = rs;
         }
 #pragma unroll
         for (int q = 0; q < TNe / 2; ++q) {
@@ -473,13 +500,18 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
           uint32_t off = lane_off;
           asm volatile("" : "+v"(off));
           off += (uint32_t)((i * MF * N + 32 * q) * 2);
-          if (lane_row < cur_t.M - i * MF && n0 + wne * WNe + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
+          if (lane_row < cur_t.M - i * MF && n0 + c0 + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
         }
       }
     };
-    const bool cur_half = cur_t.M <= BM / 2;  // uniform
-    if (cur_half) epilogue(std::true_type{});
-    else epilogue(std::false_type{});
+    const int cur_mode = tile_mode(cur_t.M, cur_t.nt);  // uniform
+    if (cur_mode == M_HALF_H) {
+      epilogue(std::integral_constant<int, M_HALF_H>{});
+    } else if (cur_mode == M_HALF_W) {
+      if constexpr (kHalfW) epilogue(std::integral_constant<int, M_HALF_W>{});
+    } else {
+      epilogue(std::integral_constant<int, M_FULL>{});
+    }
     // every wave has read this tile's bias and written its row sums: the
     // next tile's bias may land, the sums may be added.  LDS only, so the
     // barrier waits for LDS accesses alone (__syncthreads would also wait
@@ -488,14 +520,18 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     slab_barrier();
     if (want_sq) {
       // the wave columns' partial sums in column order (half-height tiles
-      // add four, so their sums round differently from a full tile's).  The
-      // empty asm keeps the row's LDS addresses from being formed at kernel
-      // start and kept (spilled) through the K loop.
+      // add four, so their sums round differently from a full tile's; a
+      // half-width tile has one, the full tile's first, its second being
+      // past N).  The empty asm keeps the row's LDS addresses from being
+      // formed at kernel start and kept (spilled) through the K loop.
       int m0 = tid;
       asm volatile("" : "+v"(m0));
-      if (cur_half)
+      if (cur_mode == M_HALF_H)
         for (int m = m0; m < cur_t.M; m += C::NT)
           p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = ((s_sq[0][m] + s_sq[1][m]) + s_sq[2][m]) + s_sq[3][m];
+      else if (cur_mode == M_HALF_W)
+        for (int m = m0; m < cur_t.M; m += C::NT)
+          p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = s_sq[0][m];
       else
         for (int m = m0; m < cur_t.M; m += C::NT)
           p.sq_part[(cur_t.row0 + m) * (int64_t)n_tiles + cur_t.nt] = s_sq[0][m] + s_sq[1][m];

@@ -467,11 +467,14 @@ hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
   // 64-wide 2-stage ring 1009, no ping-pong 986, ping-pong on half stages of
   // a 2-stage 64-wide ring 667).  Neither is bound by the matrix pipe: the
   // waves stall on operand reads, stage loads and the per-tile epilogue.
-  // 256 x 256 tiles whose N is a multiple of 256 go to the persistent kernel
-  // (gemm_bf16_persist.hip), this one keeps the rest.
+  // 256 x 256 tiles go to the persistent kernel (gemm_bf16_persist.hip)
+  // where it supports the pass; this one keeps the rest.  (With its half-
+  // height and half-width tile modes the persistent kernel also took the
+  // fine-grained up pass, N = 1408, from 385 to 357 us before the half-width
+  // mode.)
   if (tile == 513)
-    return gemm_persist_supported(a) && a.N % 256 == 0 ? launch_gemm_bf16_persist(a, st)
-                                                        : launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
+    return gemm_persist_supported(a) ? launch_gemm_bf16_persist(a, st)
+                                     : launch_v2<256, 256, 2, 4, 4, 1, 1, 16>(a, st);
   if (tile == 256) return launch_v2<256, 128, 2, 4, 3, 1, 2, 16>(a, st);
   if (tile == 144)
     return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2, 16>(a, st)

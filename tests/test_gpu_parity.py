@@ -388,15 +388,18 @@ def _torch_act(z, act):
     ([2000, 0, 2600, 300, 3500, 1800], 768, 512, True, "gelu", True),
     ([1650, 1540, 0, 2100, 1580, 1700, 1600, 1830], 2048, 544, False, "relu", False),
     ([1664, 1665, 1537, 2048, 1792], 1024, 768, True, "swish", True),
+    ([1700, 1900, 1540, 2100], 1152, 640, True, "gelu", True),
 ])
 def test_grouped_gemm_persistent_tiles(sizes, d, F, gather, act, with_sq):
     """Passes that take the persistent 256 x 256 kernel (groups of >= 1536
-    rows on average, N a multiple of 256): empty, partial and many-tile
+    rows on average, N at least 512): empty, partial and many-tile
     groups, rows gathered through a row map, the row sums of squares, 64-wide
     K stages (K % 64 == 0) and, for the second shape's down pass, 32-wide
     stages (K = 544) in the N-tile-major order (N G > rows); last row tiles
     of at most 128 rows take the half-height mode (the third shape puts
-    128, 129 and 1 rows there).  Every row of
+    128, 129 and 1 rows there), last column tiles of at most 128 columns the
+    half-width mode (the fourth shape: N = 640 up, 1152 down, both with 128
+    columns in the last tile, beside half-height tiles).  Every row of
     both passes against a float32 product of the same bf16 operands, the row
     sums of squares against the float32 activations, and two runs agree bit
     for bit (each block walks a list of tiles; a race between one tile's
