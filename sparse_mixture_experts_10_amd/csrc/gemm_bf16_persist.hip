@@ -12,6 +12,10 @@
 //    reads the next step into the other and issues the global -> LDS loads
 //    (global_load_lds_dwordx4) of the stage NS ahead into the buffer the
 //    previous stage left, one barrier per stage;
+//  * a tile of at most 128 rows runs half-height (the four waves side by
+//    side along N, 128 x 64 each) and one of at most 128 valid columns
+//    half-width (stacked along M, 64 x 128 each): half the MFMAs, the same
+//    loads;
 //  * between tiles, the next tile's first NS stages are issued before the
 //    finished tile's epilogue runs, so their latency hides behind it;
 //  * the epilogue is per wave: bias (staged in LDS during the tile's K
