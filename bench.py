@@ -135,11 +135,16 @@ def ceilings():
 
 
 def gemm_source_tag() -> str:
-    import hashlib
+    """Hash of the grouped GEMM's sources with comments and blank space taken
+    out, so a counter summary stays matched through comment-only edits."""
+    import hashlib, re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_10_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_10_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
