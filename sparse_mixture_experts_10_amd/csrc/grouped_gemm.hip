@@ -224,10 +224,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs p) {
 //        tiles, or groups of >= 1536 rows (the weight tiles are re-read from
 //        L2 the fewest times; measured on MI355X against the 64-wide 2-stage
 //        ring it replaces: the two shared experts of the fine-grained layer,
-//        d 2048, F 1408, 8192 rows, 218 -> 186 us); when N is a multiple of
-//        256 and K has one segment, the persistent four-wave kernel instead
+//        d 2048, F 1408, 8192 rows, 218 -> 186 us); when K has one segment
+//        and the output is bf16, the persistent four-wave kernel instead
 //        (gemm_bf16_persist.hip; 128 groups of 2048 rows at d 4096, F 1536:
-//        up 1047 -> 1091, down 1034 -> 1109 TFLOP/s)
+//        up 1047 -> 1091, down 1034 -> 1109 TFLOP/s; with its half-width
+//        mode also N = 1408, the fine-grained up pass, 380 -> 345 us)
 // Between 128 and 144 rows, for passes of at most four waves of 128-row tiles,
 // the one that puts the fewest rows on the busiest CU wins, with every group
 // assumed to hold its mean share plus 8 % (routing imbalance).  A group of up to 1152 rows then takes eight 144-row tiles
