@@ -76,7 +76,10 @@ class MoELayer:
     the routed path (forward only; calls() lists every call in order).
     overlap_stats: run the statistics call (with credit, or after the separate
     router and dispatch calls) on a second side stream beside the down pass
-    and the combine (forward only).
+    and the combine (forward only).  Off by default: the persistent down-pass
+    GEMM holds every CU, so the statistics kernels wait for its tail anyway,
+    and the fork and join cost more than they hide (large workload step
+    6742-6756 us on the main stream, 6761-6771 us on the side stream).
     """
 
     def __init__(self, W_g, W1, b1, W2, b2, *, k: int, act: str, capacity_factor=None,
@@ -84,7 +87,7 @@ class MoELayer:
                  alpha: float = 0.01, beta: float = 1e-3, credit: bool = False,
                  gather_rows: bool = True, fused_route: bool = True, noise=None, noise_std: float = 0.0,
                  temperature: float = 1.0, mlp_gate: Optional[Tuple[torch.Tensor, ...]] = None, overlap_shared: bool = True,
-                 overlap_stats: bool = True):
+                 overlap_stats: bool = False):
         self.W_g, self.b_g, self.b_sel = W_g, b_g, b_sel
         self.W1, self.b1, self.W2, self.b2 = W1, b1, W2, b2
         self.shared = shared
