@@ -162,14 +162,35 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   const int band = (total + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds;
   const int first = blockIdx.x / kXcds, step = gridDim.x / kXcds;
+  // The band's last round: when its tiles fill at most half of the XCD's
+  // blocks and the K loop is long (K >= 4096), each is dealt as two
+  // half-height pieces (rows 0 .. 127 and 128 .. 255, each in the
+  // half-height mode), so the round takes about half a tile's time on twice
+  // the blocks instead of a whole tile's on few.  (Measured on MI355X: large
+  // up pass, K 4096, 3045 -> 3029 us; with K 1408-2048 the shorter last
+  // round gained nothing, or lost up to 2 %.)
+  // A piece computes its rows exactly as the whole tile would (same K
+  // order); only its row sums of squares add four wave partials, not two.
+  const int blen = total - xcd * band < band ? (total - xcd * band > 0 ? total - xcd * band : 0) : band;
+  const int full_rounds = blen / step;
+  const int rem = blen - full_rounds * step;
+  const bool split_tail = 2 * rem <= step && K >= 4096;
+  const int vlen = split_tail ? full_rounds * step + 2 * rem : blen;
 
-  // tile of list position i of this block's band (M = 0: nothing to do
-  // there; M = -1: past the band's end)
+  // tile of position i of this block's band, counting the last round's
+  // pieces (M = 0: nothing to do there; M = -1: past the band's end)
   auto tile_at = [&](int i) {
     Tile tl;
     tl.g = 0; tl.row0 = 0; tl.M = -1; tl.nt = 0;
-    const int L = xcd * band + i;
-    if (i >= band || L >= total) return tl;
+    if (i >= vlen) return tl;
+    int piece = -1;  // 0, 1: the half of a split last-round tile
+    int ib = i;
+    if (split_tail && i >= full_rounds * step) {
+      const int v = i - full_rounds * step;
+      ib = full_rounds * step + v / 2;
+      piece = v & 1;
+    }
+    const int L = xcd * band + ib;
     const int mt = L / n_tiles;
     int lo = 0, hi = G;  // s_pre[lo] <= mt < s_pre[hi]
     while (hi - lo > 1) {
@@ -192,6 +213,14 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     tl.M = Mg - r * BM < BM ? Mg - r * BM : BM;
     if (tl.row0 >= p.max_rows) tl.M = 0;
     else if (tl.row0 + tl.M > p.max_rows) tl.M = (int)(p.max_rows - tl.row0);
+    if (piece >= 0) {
+      if (tl.M <= BM / 2) {
+        if (piece == 1) tl.M = 0;  // a half-height tile already: one piece
+      } else {
+        tl.row0 += (int64_t)piece * (BM / 2);
+        tl.M = piece ? tl.M - BM / 2 : BM / 2;
+      }
+    }
     // the same for every lane: keep it in scalar registers
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
     tl.M = __builtin_amdgcn_readfirstlane(tl.M);
