@@ -178,8 +178,9 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   const int vlen = split_tail ? full_rounds * step + 2 * rem : blen;
 
   // tile of position i of this block's band, counting the last round's
-  // pieces (M = 0: nothing to do there; M = -1: past the band's end)
-  auto tile_at = [&](int i) {
+  // pieces (M = 0: nothing to do there; M = -1: past the band's end); lane
+  // values (each lane may ask for its own i)
+  auto tile_core = [&](int i) {
     Tile tl;
     tl.g = 0; tl.row0 = 0; tl.M = -1; tl.nt = 0;
     if (i >= vlen) return tl;
@@ -195,11 +196,11 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     int lo = 0, hi = G;  // s_pre[lo] <= mt < s_pre[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= mt) lo = mid;
+      if (s_pre[mid] <= mt) lo = mid;
       else hi = mid;
     }
-    const int pre = __builtin_amdgcn_readfirstlane(s_pre[lo]);
-    const int tiles = __builtin_amdgcn_readfirstlane(s_pre[lo + 1]) - pre;
+    const int pre = s_pre[lo];
+    const int tiles = s_pre[lo + 1] - pre;
     int r = mt - pre;
     tl.nt = L - mt * n_tiles;
     if (p.n_major) {
@@ -221,7 +222,30 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
         tl.M = piece ? tl.M - BM / 2 : BM / 2;
       }
     }
-    // the same for every lane: keep it in scalar registers
+    return tl;
+  };
+  // The block's tiles, positions first, first + step, ..., looked up once
+  // into LDS by all threads together (one position a thread: a binary
+  // search over the groups each); a tile transition then reads its entry
+  // instead of searching (7 dependent LDS reads for 128 groups, about 1 % of
+  // the large down pass).  Positions past the table's end are searched.
+  constexpr int kTab = 256;
+  __shared__ int4 s_tab[kTab];
+  const int npos = vlen > first ? (vlen - first + step - 1) / step : 0;
+  for (int q = tid; q < npos && q < kTab; q += C::NT) {
+    const Tile t = tile_core(first + q * step);
+    s_tab[q] = make_int4(t.g, (int)t.row0, t.M, t.nt);
+  }
+  __syncthreads();
+  // the block's q-th tile; the same for every lane: kept in scalar registers
+  auto tile_q = [&](int q) {
+    Tile tl;
+    if (q < kTab) {
+      const int4 e = q < npos ? s_tab[q] : make_int4(0, 0, -1, 0);
+      tl.g = e.x; tl.row0 = e.y; tl.M = e.z; tl.nt = e.w;
+    } else {
+      tl = tile_core(first + q * step);
+    }
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
     tl.M = __builtin_amdgcn_readfirstlane(tl.M);
     tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
@@ -408,9 +432,9 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
   };
 
   // ---- the tile loop
-  int it = first;
-  Tile tl = tile_at(it);
-  while (tl.M == 0) tl = tile_at(it += step);
+  int it = 0;  // the block's tile count so far
+  Tile tl = tile_q(it);
+  while (tl.M == 0) tl = tile_q(++it);
   if (tl.M < 0) return;  // uniform
   set_sources(tl);
   load_bias(tl);
@@ -439,7 +463,7 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
     // harmless reloads past its end), and so has its bias: once every wave
     // is here the ring is free for the next tile's first loads
     const Tile cur_t = tl;
-    do tl = tile_at(it += step); while (tl.M == 0);
+    do tl = tile_q(++it); while (tl.M == 0);
     wait_vmcnt<0>();
     __syncthreads();
     if (tl.M > 0) {
