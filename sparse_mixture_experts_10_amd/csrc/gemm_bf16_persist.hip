@@ -20,18 +20,20 @@
 //    finished tile's epilogue runs, so their latency hides behind it;
 //  * the epilogue is per wave: bias (staged in LDS during the tile's K
 //    loop), activation, optional row sums of squares, bf16 rows written
-//    straight from registers as 16-byte stores, eight whole 128-byte row
-//    lines a store (lanes exchange pieces by permlane and DPP moves), with
-//    no block barrier until the row sums are combined.  The stores are
-//    non-temporal: the pass never reads its output again, and the output
-//    (2 GB on the large down pass) otherwise evicts the operand lines other
-//    blocks still read from the XCD's L2.  Measured on MI355X (large down
-//    pass): without any output stores the pass ran 20 % faster, with every
-//    store of an XCD aimed at one 128 KB region (no write-back, no
-//    eviction) 19 %, at an 8 MB region (eviction, no HBM writes) 10 %;
-//    whole-line non-temporal stores recover 3 % (plain stores of whole
-//    lines 2 %; agent- or system-scope stores, and non-temporal 64-byte
-//    pieces, were slower than plain 64-byte pieces).
+//    straight from registers as 16-byte stores (lanes exchange pieces by
+//    permlane moves), with no block barrier until the row sums are
+//    combined.  Outputs larger than the 256 MB Infinity Cache are stored
+//    as eight whole 128-byte row lines a store (a further DPP exchange)
+//    with the non-temporal hint: the pass never reads its output again,
+//    and an output of gigabytes otherwise evicts the operand lines other
+//    blocks still read from the XCD's L2 and competes for HBM.  Measured
+//    on MI355X (large down pass, 2.1 GB out): without any output stores
+//    the pass ran 20 % faster, with every store of an XCD aimed at one
+//    128 KB region (no write-back, no eviction) 19 %, at an 8 MB region
+//    (eviction, no HBM writes) 10 %; whole-line non-temporal stores gained
+//    1-3 % over plain 64-byte row pieces (agent- or system-scope stores, and
+//    non-temporal 64-byte pieces, were slower).  Smaller outputs, read back
+//    from that cache by the next pass, keep plain 64-byte row pieces.
 // The accumulation order over K is the same as every other configuration's
 // (32-wide steps in order, each one MFMA), so C is bit-identical to theirs.
 // Measured on MI355X (128 groups of 2048 rows, d 4096, F 1536): a non-
@@ -84,7 +86,9 @@ __device__ __forceinline__ float acc_read(float a) {
   return v;
 }
 
-template <int SUB, int ACT>
+// NTS: outputs stored as whole 128-byte lines with the non-temporal hint
+// (large outputs), else as plain 64-byte row pieces.
+template <int SUB, int ACT, bool NTS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void gemm_bf16_persist_kernel(GemmArgs p) {
   using C = PCfg<SUB>;
@@ -521,9 +525,12 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
       // lane's fixed row against a uniform bound.
       char* const cbase = (char*)((bf16_t*)p.C + cur_t.row0 * (int64_t)N + n0);
       // the lane's store columns (before + 64 p2) and row (before + 8 h)
-      const int colbase = ((fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc) + 32 * (fr >> 3);
-      const uint32_t lane_off = (uint32_t)(((r0 + (fr & 7)) * N + c0 + colbase) * 2);
-      const int lane_row = r0 + (fr & 7);
+      // the lane's store row and columns (whole lines: before + 8 h, + 64 p2;
+      // row pieces: before + 32 q)
+      const int colbase = ((fc & 1) ? 16 + 4 * (fc - 1) : 4 * fc) + (NTS ? 32 * (fr >> 3) : 0);
+      const int lrow = NTS ? (fr & 7) : fr;
+      const uint32_t lane_off = (uint32_t)(((r0 + lrow) * N + c0 + colbase) * 2);
+      const int lane_row = r0 + lrow;
 #pragma unroll
       for (int i = 0; i < TMe; ++i) {
         // one row tile at a time: kept from hoisting the next tile's
@@ -549,44 +556,60 @@ void gemm_bf16_persist_kernel(GemmArgs p) {
           rs += __int_as_float(xor_lane<32>(__float_as_int(rs)));
           if (fc == 0) s_sq[sq_col][r0 + i * MF + fr] = rs;
         }
+        if constexpr (NTS) {
 #pragma unroll
-        for (int p2 = 0; p2 < TNe / 4; ++p2) {
-          // permlane16_swap(X, Y) trades X's rows 1, 3 for Y's rows 0, 2
-          // (rows of 16 lanes): even rows end with [X, partner's X], odd rows
-          // with [partner's Y, Y] -- 8 columns of the lane's row, at
-          // colbase + 32 q, for q = 2 p2 (v[0]) and 2 p2 + 1 (v[1])
-          u32x4_t v[2];
+          for (int p2 = 0; p2 < TNe / 4; ++p2) {
+            // permlane16_swap(X, Y) trades X's rows 1, 3 for Y's rows 0, 2
+            // (rows of 16 lanes): even rows end with [X, partner's X], odd rows
+            // with [partner's Y, Y] -- 8 columns of the lane's row, at
+            // colbase + 32 q, for q = 2 p2 (v[0]) and 2 p2 + 1 (v[1])
+            u32x4_t v[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int q = 2 * p2 + h;
+            for (int h = 0; h < 2; ++h) {
+              const int q = 2 * p2 + h;
+              const auto w0 = __builtin_amdgcn_permlane16_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
+              const auto w1 = __builtin_amdgcn_permlane16_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
+              v[h] = u32x4_t{w0[0], w1[0], w0[1], w1[1]};
+            }
+            // Whole 128-byte lines: lanes fr and fr ^ 8 (row_ror:8 inside each
+            // 16-lane row) trade pieces so that the first store holds rows
+            // 0 .. 7 of the slice and the second rows 8 .. 15, each row's 64
+            // columns 64 p2 .. + 63 from eight lanes (fr < 8: q = 2 p2, fr >= 8:
+            // q = 2 p2 + 1).  The bank masks pick the lanes that take their
+            // partner's piece (banks 2, 3 are lanes 8 .. 15 of a row).
+            u32x4_t s[2];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              s[0][d] = __builtin_amdgcn_update_dpp(v[0][d], v[1][d], 0x128, 0xF, 0xC, false);
+              s[1][d] = __builtin_amdgcn_update_dpp(v[1][d], v[0][d], 0x128, 0xF, 0x3, false);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              // formed here: the empty asm keeps the offset from being computed
+              // (and kept live) ahead of time
+              uint32_t off = lane_off;
+              asm volatile("" : "+v"(off));
+              off += (uint32_t)(((i * MF + 8 * h) * N + 64 * p2) * 2);
+              // Non-temporal: the output is not read again in this pass.
+              if (lane_row + 8 * h < cur_t.M - i * MF && n0 + c0 + colbase + 64 * p2 < N)
+                __builtin_nontemporal_store(s[h], (u32x4_t*)(cbase + off));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < TNe / 2; ++q) {
+            // the 8 columns of the lane's row at colbase + 32 q (as above)
             const auto w0 = __builtin_amdgcn_permlane16_swap(pk[2 * q][0], pk[2 * q + 1][0], false, false);
             const auto w1 = __builtin_amdgcn_permlane16_swap(pk[2 * q][1], pk[2 * q + 1][1], false, false);
-            v[h] = u32x4_t{w0[0], w1[0], w0[1], w1[1]};
-          }
-          // Whole 128-byte lines: lanes fr and fr ^ 8 (row_ror:8 inside each
-          // 16-lane row) trade pieces so that the first store holds rows
-          // 0 .. 7 of the slice and the second rows 8 .. 15, each row's 64
-          // columns 64 p2 .. + 63 from eight lanes (fr < 8: q = 2 p2, fr >= 8:
-          // q = 2 p2 + 1).  The bank masks pick the lanes that take their
-          // partner's piece (banks 2, 3 are lanes 8 .. 15 of a row).
-          u32x4_t s[2];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            s[0][d] = __builtin_amdgcn_update_dpp(v[0][d], v[1][d], 0x128, 0xF, 0xC, false);
-            s[1][d] = __builtin_amdgcn_update_dpp(v[1][d], v[0][d], 0x128, 0xF, 0x3, false);
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            // formed here: the empty asm keeps the offset from being computed
-            // (and kept live) ahead of time
+            vec16 val;
+            val.w[0] = w0[0];
+            val.w[1] = w1[0];
+            val.w[2] = w0[1];
+            val.w[3] = w1[1];
             uint32_t off = lane_off;
             asm volatile("" : "+v"(off));
-            off += (uint32_t)(((i * MF + 8 * h) * N + 64 * p2) * 2);
-            // Non-temporal: the output is not read again in this pass; with
-            // whole lines per store this measured 3 % faster on the large
-            // down pass than plain stores (64-byte pieces with nt: slower).
-            if (lane_row + 8 * h < cur_t.M - i * MF && n0 + c0 + colbase + 64 * p2 < N)
-              __builtin_nontemporal_store(s[h], (u32x4_t*)(cbase + off));
+            off += (uint32_t)((i * MF * N + 32 * q) * 2);
+            if (lane_row < cur_t.M - i * MF && n0 + c0 + colbase + 32 * q < N) *(vec16*)(cbase + off) = val;
           }
         }
       }
@@ -635,8 +658,16 @@ static hipError_t launch_persist(const GemmArgs& a, hipStream_t st) {
   const int64_t mt = (rows + 255) / 256 + (a.group_offset ? a.G : 0);
   const int64_t bound = grid_blocks(mt, (a.N + 255) / 256);
   const int64_t blocks = bound < kCus ? bound : kCus;  // a multiple of 8 either way
-#define MOE_PERSIST(ACTV) \
-  hipLaunchKernelGGL((gemm_bf16_persist_kernel<SUB, ACTV>), dim3((unsigned)blocks), dim3(256), 0, st, a)
+  // Outputs beyond the 256 MB Infinity Cache (the large layer's 0.8 and
+  // 2.1 GB) go out as whole non-temporal lines; smaller ones (read back by
+  // the next pass from that cache) as plain row pieces, which measured 2-3 %
+  // faster there (64-expert layers, outputs of 33-201 MB).
+  const bool nts = rows * (int64_t)a.N * 2 > ((int64_t)256 << 20);
+#define MOE_PERSIST(ACTV)                                                                                         \
+  do {                                                                                                           \
+    if (nts) hipLaunchKernelGGL((gemm_bf16_persist_kernel<SUB, ACTV, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);  \
+    else hipLaunchKernelGGL((gemm_bf16_persist_kernel<SUB, ACTV, false>), dim3((unsigned)blocks), dim3(256), 0, st, a); \
+  } while (0)
   switch (a.act) {
     case ACT_RELU: MOE_PERSIST(ACT_RELU); break;
     case ACT_GELU: MOE_PERSIST(ACT_GELU); break;

@@ -451,6 +451,74 @@ def test_grouped_gemm_persistent_tiles(sizes, d, F, gather, act, with_sq):
     close_out(f64(out), torch.cat(want_o).double().cpu().numpy(), "bf16", "down pass, persistent tiles")
 
 
+def test_grouped_gemm_persistent_large_outputs():
+    """Passes whose output exceeds the 256 MB Infinity Cache store whole
+    128-byte row lines with the non-temporal hint (lanes trade pieces across
+    rows); smaller ones store 64-byte row pieces.  Here 128730 gathered rows
+    over six groups (one empty), d 1152, F 1408: the up pass writes 362 MB,
+    the down pass 297 MB, both with N = 128 past a multiple of 256 (the
+    half-width mode) and last row tiles of 33, 48, 96 (half-height), 129 and
+    168 rows.  Every group's rows must equal, bit for bit, the same group
+    run alone (an output under the cache: the row-piece stores), with the
+    row sums of squares; the whole pass is also checked against a float32
+    product of the same operands (on the GPU) and against a second run."""
+    sizes = [30000, 0, 28000, 25729, 20001, 25000]
+    d, F, n_src = 1152, 1408, 5000
+    G = len(sizes)
+    off = torch.zeros(G + 1, dtype=torch.int32)
+    off[1:] = torch.cumsum(torch.tensor(sizes), 0)
+    rows = int(off[-1])
+    assert rows * F * 2 > 256 << 20 and rows * d * 2 > 256 << 20
+    say(f"[gpu] persistent grouped gemm, large outputs: G={G} rows={rows} d={d} F={F}")
+    g = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.randn(n_src, d, device="cuda", generator=g).to(torch.bfloat16)
+    rmap = torch.randint(0, n_src, (rows,), device="cuda", generator=g).to(torch.int32)
+    W1 = (torch.randn(G, F, d, device="cuda", generator=g) / d ** 0.5).to(torch.bfloat16)
+    b1 = (0.1 * torch.randn(G, F, device="cuda", generator=g)).to(torch.bfloat16)
+    W2 = (torch.randn(G, d, F, device="cuda", generator=g) / F ** 0.5).to(torch.bfloat16)
+    b2 = (0.1 * torch.randn(G, d, device="cuda", generator=g)).to(torch.bfloat16)
+
+    def run(goff, nrows, w1, bb1, w2, bb2, rm):
+        ws = torch.empty(api.moe_workspace_bytes(api.OP_FFN, F=F, max_rows=nrows), dtype=torch.uint8,
+                         device="cuda")
+        hid = torch.zeros(nrows, F, dtype=torch.bfloat16, device="cuda")
+        sq = torch.zeros(nrows, dtype=torch.float32, device="cuda")
+        out = torch.zeros(nrows, d, dtype=torch.bfloat16, device="cuda")
+        api.moe_expert_up(x, goff, nrows, w1, bb1, "gelu", hid, sq, ws, a_rows=rm)
+        api.moe_expert_down(hid, goff, nrows, w2, bb2, out)
+        return hid, sq, out
+
+    big = run(off.cuda(), rows, W1, b1, W2, b2, rmap)
+    again = run(off.cuda(), rows, W1, b1, W2, b2, rmap)
+    torch.cuda.synchronize()
+    for u, v in zip(again, big):
+        assert torch.equal(u.view(torch.int32 if u.dtype == torch.float32 else torch.int16),
+                           v.view(torch.int32 if v.dtype == torch.float32 else torch.int16))
+    hid, sq, out = big
+    for gi in range(G):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        if r1 == r0:
+            continue
+        say(f"[gpu]   group {gi} alone: {r1 - r0} rows")
+        one = torch.tensor([0, r1 - r0], dtype=torch.int32, device="cuda")
+        h1, s1, o1 = run(one, r1 - r0, W1[gi:gi + 1].contiguous(), b1[gi:gi + 1].contiguous(),
+                         W2[gi:gi + 1].contiguous(), b2[gi:gi + 1].contiguous(), rmap[r0:r1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(h1.view(torch.int16), hid[r0:r1].view(torch.int16)), f"group {gi}: hidden"
+        assert torch.equal(s1.view(torch.int32), sq[r0:r1].view(torch.int32)), f"group {gi}: row sums"
+        assert torch.equal(o1.view(torch.int16), out[r0:r1].view(torch.int16)), f"group {gi}: output"
+        a = x[rmap[r0:r1].long()].float()
+        h = _torch_act(a @ W1[gi].float().t().contiguous() + b1[gi].float(), "gelu")
+        o = hid[r0:r1].float() @ W2[gi].float().t().contiguous() + b2[gi].float()
+        for got, want, what in ((hid[r0:r1], h, "up"), (out[r0:r1], o, "down")):
+            err = (got.double() - want.double())
+            maxabs = float(err.abs().max())
+            relf = float(err.norm() / want.double().norm())
+            assert maxabs <= 2e-2 and relf <= 5e-3, f"group {gi} {what}: max-abs {maxabs:.3e} rel-F {relf:.3e}"
+        rs = (h * h).sum(1).double()
+        assert float(((sq[r0:r1].double() - rs).abs() / rs.abs().clamp(min=1e-30)).max()) <= 1e-4
+
+
 def test_shared_ffn_persistent_dense_tiles():
     """One shared expert over 3000 tokens at d 768, F 1024: both dense passes
     (no group offsets) take the persistent 256 x 256 kernel; every row against
