@@ -480,7 +480,13 @@ hipError_t launch_gemm_bf16_v2(const GemmArgs& a, int tile, hipStream_t st) {
     return gemm_v2_wide_k(a) ? launch_v2<144, 128, 3, 4, 2, 2, 2, 16>(a, st)
                              : launch_v2<144, 128, 3, 2, 3, 1, 2, 16>(a, st);
   if (tile == 145) return launch_v2<144, 128, 3, 4, 4, 2, 1, 16>(a, st);
-  if (tile == 257) return launch_v2<128, 256, 2, 4, 3, 1, 2, 16>(a, st);
+  // 128 x 256 tiles with K % 64 == 0 take 64-wide stages (whole 128-byte
+  // lines a row) in a 3-stage ring, one block a CU: the switch layer's up
+  // pass (weight rows of 2 KB streamed in K slabs) 158-160 -> 154 us against
+  // two blocks a CU on 32-wide stages
+  if (tile == 257)
+    return gemm_v2_wide_k(a) ? launch_v2<128, 256, 2, 4, 3, 2, 1, 16>(a, st)
+                             : launch_v2<128, 256, 2, 4, 3, 1, 2, 16>(a, st);
   if (tile == 259) return launch_v2<128, 128, 2, 4, 4, 2, 1, 16>(a, st);
   if (tile == 64) return launch_v2<128, 64, 2, 2, 4, 1, 2, 16>(a, st);
   return launch_v2<128, 128, 2, 4, 3, 1, 2, 16>(a, st);
