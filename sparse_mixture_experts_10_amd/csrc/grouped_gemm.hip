@@ -286,6 +286,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   a.n_major = gemm_n_major(a);
   const int t = bf16_tile(a);
+  // The persistent 256 x 256 kernel takes the N-major order for every
+  // grouped pass: with 32 blocks of an XCD walking neighbouring tiles, a
+  // round then spans few weight tiles over all of an expert's row tiles
+  // (measured on MI355X, 128 experts of 2048 rows at d 4096, F 1536: up
+  // pass 2999 -> 2956 us; the down pass is N-major by the rule above; on the
+  // 8-expert default passes, which take other kernels, N-major measured
+  // 1 % slower).
+  if (t == 513 && a.group_offset != nullptr && gemm_persist_supported(a)) a.n_major = true;
   if (t) return launch_gemm_bf16_v2(a, t, st);
   return launch_gemm_bf16_v1(a, st);
 }
