@@ -325,7 +325,9 @@ int moe_combine(const void* expert_out, const int32_t* row, const float* topk_ga
  *                    (the expert-attributed loss of panel (b), N = T)
  * Inputs: logits [T,E], lse [T], topk_idx [T,k], topk_gate [T,k], expert_count
  * [E] (device, from moe_router_topk / moe_dispatch).  Outputs f [E], P [E],
- * losses [3] fp32 device.  Credit is computed when credit and mean_credit are
+ * losses [3] fp32 device; all three may be NULL together when credit is
+ * requested (the credit alone, e.g. after moe_route computed the statistics),
+ * not one without the others.  Credit is computed when credit and mean_credit are
  * both non-NULL; it then needs hidden_sqnorm [rows], row [T,k], expert_offset
  * [E+1] and row_token [rows] (device).  The expert-attributed loss is computed
  * when token_loss [T] fp32 and expert_loss [E] fp32 (device) are both non-NULL,

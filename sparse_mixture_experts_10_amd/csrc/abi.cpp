@@ -464,9 +464,11 @@ int moe_route_stats(const float* logits, const float* lse, const int32_t* topk_i
   if (int rc = check_ek(E, k)) return rc;
   if (T < 1) return MOE_ERR_INVALID_ARG;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
-  if (!logits || !lse || !topk_idx || !topk_gate || !expert_count || !f || !P || !losses)
-    return MOE_ERR_INVALID_ARG;
+  if (!logits || !lse || !topk_idx || !topk_gate || !expert_count) return MOE_ERR_INVALID_ARG;
+  // f, P and losses go together; all NULL asks for the credit alone
+  if ((f == nullptr) != (P == nullptr) || (f == nullptr) != (losses == nullptr)) return MOE_ERR_INVALID_ARG;
   if ((credit == nullptr) != (mean_credit == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (f == nullptr && credit == nullptr) return MOE_ERR_INVALID_ARG;  // nothing to compute
   if (credit && (!hidden_sqnorm || !row || !expert_offset || !row_token)) return MOE_ERR_INVALID_ARG;
   if ((token_loss == nullptr) != (expert_loss == nullptr)) return MOE_ERR_INVALID_ARG;
   if (token_loss && !credit) return MOE_ERR_INVALID_ARG;   // the loss is weighted by the credit

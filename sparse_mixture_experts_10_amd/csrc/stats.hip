@@ -17,7 +17,9 @@
 // tokens fixed-order partial sums (fp64) of softmax mass per expert and of
 // lse^2, and writes the per-choice credit (also stored per packed row).  Kernel 2 sums the partials in
 // block order (block 0) and, in blocks 1..E, each expert's credit over its
-// packed rows in row order.
+// packed rows in row order.  With f, P and losses NULL (the routing pass
+// computed them) only the credit is formed: kernel 1 skips the partial sums
+// and block 0 of kernel 2 has nothing to do.
 
 #include "common.h"
 #include "internal.h"
@@ -34,7 +36,8 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(
   __shared__ double s_grp[4 * 256];
   const int64_t t0 = (int64_t)blockIdx.x * kStatsTokens;
   const int64_t t1 = (t0 + kStatsTokens < T) ? t0 + kStatsTokens : T;
-  stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1), s_grp);
+  if (part != nullptr)  // uniform; nullptr: the credit alone
+    stats_block_partials(logits, lse, t0, t1, E, s_red, part + (int64_t)blockIdx.x * (E + 1), s_grp);
   const int64_t t = t0 + threadIdx.x;
   if (credit != nullptr && t < t1) {
     for (int j = 0; j < k; ++j) {
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void stats_final_kernel(
   __shared__ double s_z[256];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
-    stats_finish(part, nparts, count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
+    if (f != nullptr) stats_finish(part, nparts, count, T, E, k, alpha, beta, f, Pm, losses, s_red, s_z);
     return;
   }
   const int e = blockIdx.x - 1;
@@ -109,8 +112,10 @@ hipError_t launch_stats(const float* logits, const float* lse, const int32_t* id
   (void)idx;
   (void)row_token;
   const int64_t nparts = (T + kStatsTokens - 1) / kStatsTokens;
+  // f == nullptr: the credit alone (the statistics' partial sums are skipped)
   hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)nparts), dim3(256), 0, st, logits, lse, T,
-                     E, k, gate, sq, row, credit, ws_partial, credit_row, token_loss, loss_row);
+                     E, k, gate, sq, row, credit, f != nullptr ? ws_partial : nullptr, credit_row,
+                     token_loss, loss_row);
   const unsigned nblk = mean_credit != nullptr ? (unsigned)(E + 1) : 1u;
   hipLaunchKernelGGL(stats_final_kernel, dim3(nblk), dim3(256), 0, st, ws_partial, (int)nparts, count,
                      T, E, k, alpha, beta, f, Pm, losses, offset, credit_row, mean_credit, loss_row,

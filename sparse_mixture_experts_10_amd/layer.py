@@ -270,6 +270,9 @@ class MoELayer:
         api.moe_combine(o.y_disp, o.row, o.topk_gate, o.shared_out, o.y, stream)
 
     def stats(self, o: MoEOutputs, stream=None) -> None:
+        # after the fused routing call f, P and the losses are already there:
+        # only the credit is asked for
+        fpl = (None, None, None) if self.fused else (o.f, o.P, o.losses)
         api.moe_route_stats(o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, self.alpha,
-                            self.beta, o.f, o.P, o.losses, o.sqnorm, o.row, o.expert_offset,
+                            self.beta, *fpl, o.sqnorm, o.row, o.expert_offset,
                             o.row_token, o.credit, o.mean_credit, o.ws_stats, stream)

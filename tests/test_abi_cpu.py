@@ -231,8 +231,9 @@ def test_shared_combine_stats_validation():
     assert lib.moe_combine(FAKE, FAKE, FAKE, MIS, 4, 2, 8, 1, FAKE, None) == INVALID
     assert lib.moe_combine(FAKE, FAKE, FAKE, None, 0, 2, 8, 1, FAKE, None) == OK
 
-    def stats(T=16, E=4, k=2, credit=NULL, mc=NULL, sq=NULL, tl=NULL, el=NULL, ws=FAKE, wsb=1 << 20):
-        return lib.moe_route_stats(FAKE, FAKE, FAKE, FAKE, FAKE, T, E, k, 0.01, 1e-3, FAKE, FAKE, FAKE, sq,
+    def stats(T=16, E=4, k=2, credit=NULL, mc=NULL, sq=NULL, tl=NULL, el=NULL, ws=FAKE, wsb=1 << 20,
+              f=FAKE, P=FAKE, losses=FAKE):
+        return lib.moe_route_stats(FAKE, FAKE, FAKE, FAKE, FAKE, T, E, k, 0.01, 1e-3, f, P, losses, sq,
                                    FAKE, FAKE, FAKE, credit, mc, tl, el, ws, wsb, None)
     assert stats(T=0) == INVALID
     assert stats(k=5) == INVALID
@@ -242,6 +243,9 @@ def test_shared_combine_stats_validation():
     assert stats(wsb=8) == WORKSPACE
     assert stats(tl=FAKE) == INVALID                # token_loss and expert_loss go together
     assert stats(tl=FAKE, el=FAKE) == INVALID       # the expert loss needs the credit
+    assert stats(f=NULL) == INVALID                 # f, P and losses go together
+    assert stats(P=NULL, losses=NULL) == INVALID
+    assert stats(f=NULL, P=NULL, losses=NULL) == INVALID   # and without credit nothing is asked
     assert lib.moe_balance_losses(FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 0.01, 1e-3, FAKE, FAKE, FAKE, 1 << 20,
                                   None) == INVALID
     assert lib.moe_balance_losses(FAKE, FAKE, FAKE, FAKE, 16, 4, 2, 0.01, 1e-3, FAKE, FAKE, NULL, 0,

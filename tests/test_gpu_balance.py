@@ -75,6 +75,32 @@ def test_selection_bias_update_balanced_and_edge():
     assert b.cpu().tolist() == [0.0, -0.25, 0.25, 0.0, 0.0, 0.0, 0.0, 0.0]
 
 
+def test_credit_alone_matches_full_statistics_call():
+    """moe_route_stats with f, P and losses NULL (the credit alone, as the
+    layer asks after the fused routing call) gives the same credit, mean
+    credit and expert loss, bit for bit, as the full call, and that full call
+    reproduces the routing pass's f, P and losses."""
+    w = CASES["large_credit_s"]
+    inp, layer, o, ref = run_layer(w)
+    tl_d = torch.as_tensor(synth.token_losses(w)).cuda()
+    got = {}
+    for name, fpl in (("alone", (None, None, None)),
+                      ("full", (torch.empty_like(o.f), torch.empty_like(o.P), torch.empty_like(o.losses)))):
+        cr, mc, el = torch.empty_like(o.credit), torch.empty_like(o.mean_credit), torch.empty(w.E, device="cuda")
+        api.moe_route_stats(o.logits, o.lse, o.topk_idx, o.topk_gate, o.expert_count, w.alpha, w.beta, *fpl,
+                            o.sqnorm, o.row, o.expert_offset, o.row_token, cr, mc, o.ws_stats,
+                            token_loss=tl_d, expert_loss=el)
+        torch.cuda.synchronize()
+        got[name] = (cr, mc, el, fpl)
+    for a, b in zip(got["alone"][:3], got["full"][:3]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(got["alone"][0].view(torch.int32), o.credit.view(torch.int32))
+    assert torch.equal(got["alone"][1].view(torch.int32), o.mean_credit.view(torch.int32))
+    f, P, losses = got["full"][3]
+    for a, b in ((f, o.f), (P, o.P), (losses, o.losses)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_expert_loss_and_dro_steps():
     """Expert-attributed loss from synthetic per-token losses, then three EMA /
     DRO steps, each against the oracle carrying its own state."""
